@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Throughput of the tensor-parallel layer-shard hot path on one MI355X.
+
+One step = one whole pass of the path on one batch of seeded synthetic input:
+layer forward (LN, QKV, attention, output projection, all-reduce stand-in, LN,
+fc1+GeLU, fc2, all-reduce stand-in), vocabulary-parallel cross-entropy
+forward and backward, layer backward (both blocks, both phases, and the
+backward all-reduce stand-ins). Inputs are resident in HBM before timing.
+
+Prints ONE JSON line. `value` = algorithmic flops of the step (layer shard
+fwd+bwd, causal attention counted over visible pairs only, plus the loss's
+logits fwd/dgrad/wgrad) / measured step time, in TFLOP/s.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+       python bench.py --copy-calibration     (plain copy for PMC byte scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (AMD data sheet)
+PEAK_HBM_GBS = 8000.0                           # MI355X HBM3E
+MFMA_KERNELS = {"gemm_nt", "gemm_nn", "gemm_tn", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"}
+METRIC = "TFLOP/s per TP layer-shard fwd+bwd (bf16) and % of MI355X MFMA peak"
+
+
+def step_flops(cfg, n_ranks: int) -> dict:
+    """Algorithmic flops of one pass over `n_ranks` ranks of the TP group."""
+    t = cfg.tp
+    n, h = cfg.rows, cfg.hidden
+    hr, fr, vr = h // t, cfg.ffn // t, cfg.vocab // t
+    a_r, d, s, b = cfg.heads // t, cfg.head_dim, cfg.seq, cfg.micro_batch
+    pairs = s * (s + 1) // 2 if cfg.causal else s * s
+    fwd = 2 * n * h * 3 * hr + 4 * b * a_r * pairs * d + 2 * n * hr * h + 4 * n * h * fr
+    rows = n if cfg.mask_rows is None else cfg.mask_rows
+    layer = 3 * fwd * n_ranks
+    xent = 6 * rows * vr * h * n_ranks
+    return {"layer": layer, "xent": xent, "total": layer + xent}
+
+
+def build_step(cfg):
+    import synth
+    from tensor_transformer_layer_03_amd.step import LayerStep
+    ranks = cfg.ranks()
+    rep = synth.replicated_inputs(cfg)
+    shards = {r: synth.device_shard(cfg, synth.rank_shard(cfg, r)) for r in ranks}
+    n_peers = cfg.tp - len(ranks)
+    peers = synth.peer_partials(cfg, n_peers) if n_peers else []
+    pstats = [synth.peer_stats(cfg, r) for r in range(cfg.tp) if r not in ranks]
+    return LayerStep(cfg, rep, shards, peers, pstats), ranks
+
+
+def time_loop(fn, steps, torch):
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def traced_kernels(st, steps, B, dtype):
+    """Per-kernel event timing of `steps` passes: {name: (launches, ms, work)}."""
+    import torch
+    B.tpl_trace_enable(4096)
+    for _ in range(steps):
+        st.step()
+    torch.cuda.synchronize()
+    recs = B.tpl_trace_read(4096)
+    B.tpl_trace_enable(0)
+    agg = {}
+    for name, ms, work in recs:
+        c, t, w = agg.get(name, (0, 0.0, 0.0))
+        agg[name] = (c + 1, t + ms, w + work)
+    return agg
+
+
+def roofline(agg, dtype, traffic=None):
+    name, (count, ms, work) = max(agg.items(), key=lambda kv: kv[1][1])
+    if name in MFMA_KERNELS:
+        achieved = work / (ms / 1e3) / 1e12
+        peak = PEAK_TFLOPS[dtype]
+        return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                "launches": count, "avg_launch_us": round(ms / count * 1e3, 2),
+                "flops_per_launch": work / count}
+    achieved = work / (ms / 1e3) / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "launches": count,
+            "avg_launch_us": round(ms / count * 1e3, 2), "bytes_per_launch": work / count}
+
+
+def cpu_baseline(cfg, seqs: int) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    the first `seqs` sequences of the micro-batch (every flop of those rows)."""
+    import dataclasses
+    import numpy as np
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity mask
+        threads = len(os.sched_getaffinity(0))
+    seqs = min(seqs, cfg.micro_batch)
+    small = dataclasses.replace(cfg, micro_batch=seqs,
+                                mask_rows=None if cfg.mask_rows is None else max(1, cfg.mask_rows * seqs // cfg.micro_batch))
+    ranks = small.ranks()
+    rep = synth.replicated_inputs(small)
+    shards = {r: synth.rank_shard(small, r) for r in ranks}
+    n_peers = small.tp - len(ranks)
+    peers = synth.peer_partials(small, n_peers) if n_peers else []
+    pstats = [synth.peer_stats(small, r) for r in range(small.tp) if r not in ranks]
+    prs = {r: synth.oracle_params(small, [s], rep) for r, s in shards.items()}
+    t0 = time.perf_counter()
+    O.step_reference(prs, rep.x, rep.dout, rep.targets, rep.mask, seq=small.seq, causal=small.causal,
+                     eps=small.ln_eps, tp=small.tp, vocab_r=small.vocab_r, peers=peers, peer_stats=pstats,
+                     use_mask=small.mask_rows is not None)
+    dt = time.perf_counter() - t0
+    fl = step_flops(small, len(ranks))["total"]
+    return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle pass (numpy fp64) over {seqs} of {cfg.micro_batch} sequences "
+                      f"({fl / 1e9:.0f} GFLOP in {dt:.1f} s)"}
+
+
+def copy_calibration(torch, mib=1024, reps=5):
+    """A plain device copy of known size, to scale PMC FETCH_SIZE/WRITE_SIZE."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="gpt2_355m_t1")
+    ap.add_argument("--trace-steps", type=int, default=3)
+    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: the TP group's ranks are computed on one device and the "
+              f"all-reduce is a local sum kernel; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X, gfx950)", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    import synth
+    from tensor_transformer_layer_03_amd import binding as B
+
+    cfg = synth.get_config(args.config)
+    st, ranks = build_step(cfg)
+    fl = step_flops(cfg, len(ranks))
+
+    for _ in range(args.warmup):
+        st.step()
+    ms = time_loop(st.step, args.steps, torch)
+    ms_layer = time_loop(lambda: (st.forward(), st.backward()), max(3, args.steps // 2), torch)
+    agg = traced_kernels(st, args.trace_steps, B, cfg.dtype)
+    loss = float(st.shared["loss"][0].item())
+
+    value = fl["total"] / (ms / 1e3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    kernels = sorted(((k, c, t / args.trace_steps, w) for k, (c, t, w) in agg.items()), key=lambda r: -r[2])
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded: activations N(0,1), weights N(0,sigma_w), uniform targets)",
+        "config": {
+            "workload": f"{cfg.name}: one transformer layer, hidden {cfg.hidden}, {cfg.heads} heads x "
+                        f"{cfg.head_dim}, ffn {cfg.ffn}, TP t={cfg.tp} (ranks {ranks} on this GPU), "
+                        f"seq {cfg.seq}, micro-batch {cfg.micro_batch}, vocab {cfg.vocab}, "
+                        f"{'causal' if cfg.causal else 'bidirectional'}",
+            "global_batch": cfg.micro_batch, "seq_len": cfg.seq, "parallelism": f"tp{cfg.tp} (one GPU)",
+        },
+        "pct_of_mfma_peak": round(100 * value / peak, 2),
+        "flops_per_step": fl,
+        "layer_only": {"ms": round(ms_layer, 4), "tflops": round(fl["layer"] / (ms_layer / 1e3) / 1e12, 2),
+                       "note": "layer fwd+bwd with its 4 all-reduce stand-ins, loss excluded"},
+        "loss": round(loss, 6),
+        "roofline": roofline(agg, cfg.dtype),
+        "kernels_per_step": [{"kernel": k, "launches": c // args.trace_steps, "ms": round(t, 4),
+                              ("tflops" if k in MFMA_KERNELS else "gbs"):
+                                  round(w / args.trace_steps / (t / 1e3) / (1e12 if k in MFMA_KERNELS else 1e9), 1)}
+                             for k, c, t, w in kernels],
+    }
+    if args.cpu_seqs > 0:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seqs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,3 +22,5 @@ the exact-erf GeLU form and LayerNorm epsilon 1e-5 (the pages name neither).
 """
 from .layer import *  # noqa: F401,F403
 from .layer import __all__  # noqa: F401
+from .step import step_reference  # noqa: F401,E402
+from . import compare  # noqa: F401,E402

@@ -1,0 +1,613 @@
+// Flash-style self-attention over one rank's heads (podcast page, Outline and
+// Key concepts: self-attention parallelised by heads, so each rank runs whole
+// heads with no exchange; guide page section 3.2).
+//
+// Per head and sequence: O = softmax(Q K^T / sqrt(d) (+ causal mask)) V, the
+// probabilities never leave registers; the row log-sum-exp is kept for the
+// backward. The backward is two deterministic kernels (no atomics):
+//   dK/dV: one workgroup per 128 keys, looping over query tiles;
+//   dQ:    one workgroup per 128 queries, looping over key tiles.
+//
+// Layout trick: the forward computes S^T = K Q^T with the 32x32 MFMA, so the
+// accumulator lane l owns query l%32 and 16 keys. Online-softmax statistics
+// are then per lane (one cross-half shuffle, lane ^ 32), the O rescale is a
+// lane-uniform multiply, and the probabilities feed O^T = V^T P^T directly as
+// the MFMA B operand. The 16 keys of a lane are not contiguous, so V^T is
+// stored in LDS with key positions permuted (bits 2 and 3 of the key offset
+// inside each 16-key group swapped); a lane then reads its 8 keys with one
+// 16-byte LDS load. The same holds for K^T (dQ) and for Q^T, dO^T (dK/dV,
+// where the roles of queries and keys swap).
+#include "common.h"
+#include "kernels.h"
+
+namespace tpl {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct Args {
+  const char* qkv; int64_t ld_qkv;
+  char* ctx; int64_t ld_ctx;
+  float* lse;
+  const char* dctx;
+  char* dqkv;
+  float* delta;
+  int batch, heads, seq;
+};
+
+// Row tile: ROWS rows x D elements from global into LDS [ROWS][D + pad].
+template <typename T, int D, int ROWS, int NT>
+struct RowTile {
+  static constexpr int kVec = 16 / sizeof(T);
+  static constexpr int kLd = D + kVec;
+  static constexpr int kCpr = D / kVec;
+  static constexpr int kTotal = ROWS * kCpr;
+  static constexpr int kPer = (kTotal + NT - 1) / NT;
+  u32x4 r[kPer];
+  // base points at element (row 0, col 0) of the head; rows >= nrows read as 0.
+  __device__ __forceinline__ void load(const T* base, int64_t ld, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int idx = tid + i * NT;
+      int row = idx / kCpr, c = idx % kCpr;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (idx < kTotal && row0 + row < nrows) v = ld16(base + (int64_t)(row0 + row) * ld + c * kVec);
+      r[i] = v;
+    }
+  }
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int idx = tid + i * NT;
+      if (idx >= kTotal) break;
+      int row = idx / kCpr, c = idx % kCpr;
+      st16(lds + row * kLd + c * kVec, r[i]);
+    }
+  }
+};
+
+// Transposed tile: 64 rows x D elements from global into LDS [D][64 + pad]
+// with row positions permuted within each 16-row group (bits 2,3 swapped), so
+// the 8 rows {16q+4h+0..3, 16q+8+4h+0..3} land at positions 16q+8h+0..7.
+template <typename T, int D, int NT>
+struct TransTile {
+  static constexpr int kVec = 16 / sizeof(T);
+  static constexpr int kLd = 64 + kVec;
+  static constexpr int kUnits = 8 * (D / kVec);
+  static constexpr int kPer = (kUnits + NT - 1) / NT;
+  u32x4 r[kPer][8];
+  __device__ __forceinline__ static int row_of(int kg, int e) {
+    const int q = kg >> 1, h = kg & 1;
+    return 16 * q + (e < 4 ? 4 * h + e : 8 + 4 * h + (e - 4));
+  }
+  __device__ __forceinline__ void load(const T* base, int64_t ld, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      int unit = tid + u * NT;
+      int dv = unit % (D / kVec), kg = unit / (D / kVec);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int row = row0 + row_of(kg, e);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (unit < kUnits && row < nrows) v = ld16(base + (int64_t)row * ld + dv * kVec);
+        r[u][e] = v;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      int unit = tid + u * NT;
+      if (unit >= kUnits) break;
+      int dv = unit % (D / kVec), kg = unit / (D / kVec);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+          u32x4 o;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) o[p] = __builtin_amdgcn_perm(r[u][2 * p + 1][c >> 1], r[u][2 * p][c >> 1], sel);
+          st16(lds + (dv * 8 + c) * kLd + 8 * kg, o);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          u32x4 lo = {r[u][0][c], r[u][1][c], r[u][2][c], r[u][3][c]};
+          u32x4 hi = {r[u][4][c], r[u][5][c], r[u][6][c], r[u][7][c]};
+          T* p = lds + (dv * 4 + c) * kLd + 8 * kg;
+          st16(p, lo);
+          st16(p + 4, hi);
+        }
+      }
+    }
+  }
+};
+
+// Fragment of 8 values taken from accumulator `acc` slots base..base+7.
+template <typename T>
+__device__ __forceinline__ void acc_frag(Frag8<T>& f, const f32x16& acc, int base) {
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = acc[base + e];
+  frag_from_f32(f, v);
+}
+
+// Store a transposed accumulator tile: lane owns row `row` (query or key) and
+// d = dt*32 + 8*(r/4) + 4*grp + r%4.
+template <typename T, int D>
+__device__ __forceinline__ void store_rows(T* base, int64_t ld, int row, const f32x16* acc, float scale, int grp) {
+  T* p = base + (int64_t)row * ld;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = dt * 32 + 8 * q + 4 * grp;
+      store4(p + d, acc[dt][4 * q] * scale, acc[dt][4 * q + 1] * scale, acc[dt][4 * q + 2] * scale,
+             acc[dt][4 * q + 3] * scale);
+    }
+}
+
+// ------------------------------------------------------------------ forward
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(Args a) {
+  constexpr int NT = 256, BQ = 128, BKV = 64;
+  using KT = RowTile<T, D, BKV, NT>;
+  using VT = TransTile<T, D, NT>;
+  __shared__ __attribute__((aligned(16))) T sK[2][BKV * KT::kLd];
+  __shared__ __attribute__((aligned(16))) T sVt[2][D * VT::kLd];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
+  const int qb = gridDim.x - 1 - blockIdx.x;   // heaviest causal blocks first
+  const int b = blockIdx.y / a.heads, hd = blockIdx.y % a.heads;
+  const int s = a.seq;
+  const int hr = a.heads * D;
+  const T* Qg = reinterpret_cast<const T*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
+  const T* Kg = Qg + hr;
+  const T* Vg = Qg + 2 * hr;
+  const int q0 = qb * BQ, q0w = q0 + wave * 32, my_q = q0w + l32;
+  const float c = kLog2e * rsqrtf((float)D);
+
+  Frag8<T> qf[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    if (my_q < s) load_frag(qf[st], Qg + (int64_t)my_q * a.ld_qkv + st * 16 + grp * 8);
+    else { float z[8] = {0, 0, 0, 0, 0, 0, 0, 0}; frag_from_f32(qf[st], z); }
+  }
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  const int kv_end = CAUSAL ? min(s, q0 + BQ) : s;
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  KT kt_ld;
+  VT vt_ld;
+  kt_ld.load(Kg, a.ld_qkv, 0, s, tid);
+  vt_ld.load(Vg, a.ld_qkv, 0, s, tid);
+  kt_ld.store(sK[0], tid);
+  vt_ld.store(sVt[0], tid);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1, kv0 = t * BKV;
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      kt_ld.load(Kg, a.ld_qkv, kv0 + BKV, s, tid);
+      vt_ld.load(Vg, a.ld_qkv, kv0 + BKV, s, tid);
+    }
+    if (!CAUSAL || kv0 <= q0w + 31) {
+      f32x16 sc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kt][r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+          Frag8<T> kf;
+          load_frag(kf, &sK[cur][(kt * 32 + l32) * KT::kLd + st * 16 + grp * 8]);
+          mfma_step(sc[kt], kf, qf[st]);
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
+          float v = sc[kt][r] * c;
+          if (key >= s || (CAUSAL && key > my_q)) v = -INFINITY;
+          sc[kt][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m - m_use);
+      float sum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2f(sc[kt][r] - m_use);
+          sc[kt][r] = p;
+          sum += p;
+        }
+      sum += __shfl_xor(sum, 32, kWave);
+      l = l * alpha + sum;
+      m = m_new;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        Frag8<T> pf;
+        acc_frag(pf, sc[ks >> 1], 8 * (ks & 1));
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          Frag8<T> vf;
+          load_frag(vf, &sVt[cur][(dt * 32 + l32) * VT::kLd + ks * 16 + grp * 8]);
+          mfma_step(o[dt], vf, pf);
+        }
+      }
+    }
+    if (more) {
+      kt_ld.store(sK[cur ^ 1], tid);
+      vt_ld.store(sVt[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  if (my_q < s) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    T* Og = reinterpret_cast<T*>(a.ctx) + (int64_t)b * s * a.ld_ctx + hd * D;
+    store_rows<T, D>(Og, a.ld_ctx, my_q, o, inv, grp);
+    if (grp == 0) a.lse[((int64_t)b * a.heads + hd) * s + my_q] = m * kLn2 + logf(l);
+  }
+}
+
+// ------------------------------------------------------------------ backward prologue
+// delta[b][h][q] = sum_d dO[q][d] * O[q][d]  (= sum_j P_qj dP_qj)
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_bwd_pre_kernel(Args a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.batch * a.heads * a.seq;
+  if (idx >= total) return;
+  const int q = idx % a.seq;
+  const int hd = (idx / a.seq) % a.heads;
+  const int b = idx / ((int64_t)a.seq * a.heads);
+  const int64_t row = (int64_t)b * a.seq + q;
+  const T* o = reinterpret_cast<const T*>(a.ctx) + row * a.ld_ctx + hd * D;
+  const T* d = reinterpret_cast<const T*>(a.dctx) + row * a.ld_ctx + hd * D;
+  float acc = 0.f;
+  constexpr int kVec = 16 / sizeof(T);
+#pragma unroll
+  for (int i = 0; i < D; i += kVec) {
+    Vec16<T> vo, vd;
+    vo.raw = ld16(o + i);
+    vd.raw = ld16(d + i);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) acc += to_f32(vo.get(e)) * to_f32(vd.get(e));
+  }
+  a.delta[idx] = acc;
+}
+
+// ------------------------------------------------------------------ backward: dQ
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(Args a) {
+  constexpr int NT = 256, BQ = 128, BKV = 64;
+  using KT = RowTile<T, D, BKV, NT>;
+  using TT = TransTile<T, D, NT>;
+  __shared__ __attribute__((aligned(16))) T sK[2][BKV * KT::kLd];
+  __shared__ __attribute__((aligned(16))) T sV[2][BKV * KT::kLd];
+  __shared__ __attribute__((aligned(16))) T sKt[2][D * TT::kLd];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
+  const int qb = gridDim.x - 1 - blockIdx.x;
+  const int b = blockIdx.y / a.heads, hd = blockIdx.y % a.heads;
+  const int s = a.seq, hr = a.heads * D;
+  const T* Qg = reinterpret_cast<const T*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
+  const T* Kg = Qg + hr;
+  const T* Vg = Qg + 2 * hr;
+  const T* dOg = reinterpret_cast<const T*>(a.dctx) + (int64_t)b * s * a.ld_ctx + hd * D;
+  const int q0 = qb * BQ, q0w = q0 + wave * 32, my_q = q0w + l32;
+  const float c = kLog2e * rsqrtf((float)D);
+  const int64_t stat = ((int64_t)b * a.heads + hd) * s;
+  const float lse_q = my_q < s ? a.lse[stat + my_q] * kLog2e : 0.f;
+  const float delta_q = my_q < s ? a.delta[stat + my_q] : 0.f;
+
+  Frag8<T> qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    if (my_q < s) {
+      load_frag(qf[st], Qg + (int64_t)my_q * a.ld_qkv + st * 16 + grp * 8);
+      load_frag(df[st], dOg + (int64_t)my_q * a.ld_ctx + st * 16 + grp * 8);
+    } else {
+      float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      frag_from_f32(qf[st], z);
+      frag_from_f32(df[st], z);
+    }
+  }
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[dt][r] = 0.f;
+
+  const int kv_end = CAUSAL ? min(s, q0 + BQ) : s;
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  KT k_ld, v_ld;
+  TT kt_ld;
+  k_ld.load(Kg, a.ld_qkv, 0, s, tid);
+  v_ld.load(Vg, a.ld_qkv, 0, s, tid);
+  kt_ld.load(Kg, a.ld_qkv, 0, s, tid);
+  k_ld.store(sK[0], tid);
+  v_ld.store(sV[0], tid);
+  kt_ld.store(sKt[0], tid);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1, kv0 = t * BKV;
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      k_ld.load(Kg, a.ld_qkv, kv0 + BKV, s, tid);
+      v_ld.load(Vg, a.ld_qkv, kv0 + BKV, s, tid);
+      kt_ld.load(Kg, a.ld_qkv, kv0 + BKV, s, tid);
+    }
+    if (!CAUSAL || kv0 <= q0w + 31) {
+      f32x16 sc[2], dp[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { sc[kt][r] = 0.f; dp[kt][r] = 0.f; }
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+          Frag8<T> kf, vf;
+          load_frag(kf, &sK[cur][(kt * 32 + l32) * KT::kLd + st * 16 + grp * 8]);
+          load_frag(vf, &sV[cur][(kt * 32 + l32) * KT::kLd + st * 16 + grp * 8]);
+          mfma_step(sc[kt], kf, qf[st]);
+          mfma_step(dp[kt], vf, df[st]);
+        }
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
+          const bool ok = key < s && (!CAUSAL || key <= my_q) && my_q < s;
+          const float p = ok ? exp2f(sc[kt][r] * c - lse_q) : 0.f;
+          sc[kt][r] = p * (dp[kt][r] - delta_q);   // dS^T
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        Frag8<T> sf;
+        acc_frag(sf, sc[ks >> 1], 8 * (ks & 1));
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          Frag8<T> kf;
+          load_frag(kf, &sKt[cur][(dt * 32 + l32) * TT::kLd + ks * 16 + grp * 8]);
+          mfma_step(dq[dt], kf, sf);
+        }
+      }
+    }
+    if (more) {
+      k_ld.store(sK[cur ^ 1], tid);
+      v_ld.store(sV[cur ^ 1], tid);
+      kt_ld.store(sKt[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+  if (my_q < s) {
+    T* dQg = reinterpret_cast<T*>(a.dqkv) + (int64_t)b * s * a.ld_qkv + hd * D;
+    store_rows<T, D>(dQg, a.ld_qkv, my_q, dq, rsqrtf((float)D), grp);
+  }
+}
+
+// ------------------------------------------------------------------ backward: dK, dV
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(Args a) {
+  constexpr int NT = 256, BKB = 128, BQ = 64;
+  using RT = RowTile<T, D, BQ, NT>;
+  using TT = TransTile<T, D, NT>;
+  __shared__ __attribute__((aligned(16))) T sQ[2][BQ * RT::kLd];
+  __shared__ __attribute__((aligned(16))) T sdO[2][BQ * RT::kLd];
+  __shared__ __attribute__((aligned(16))) T sQt[2][D * TT::kLd];
+  __shared__ __attribute__((aligned(16))) T sdOt[2][D * TT::kLd];
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sDl[2][BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
+  const int b = blockIdx.y / a.heads, hd = blockIdx.y % a.heads;
+  const int s = a.seq, hr = a.heads * D;
+  const T* Qg = reinterpret_cast<const T*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
+  const T* Kg = Qg + hr;
+  const T* Vg = Qg + 2 * hr;
+  const T* dOg = reinterpret_cast<const T*>(a.dctx) + (int64_t)b * s * a.ld_ctx + hd * D;
+  const int64_t stat = ((int64_t)b * a.heads + hd) * s;
+  const int k0 = blockIdx.x * BKB, k0w = k0 + wave * 32, my_k = k0w + l32;
+  const float c = kLog2e * rsqrtf((float)D);
+
+  Frag8<T> kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    if (my_k < s) {
+      load_frag(kf[st], Kg + (int64_t)my_k * a.ld_qkv + st * 16 + grp * 8);
+      load_frag(vf[st], Vg + (int64_t)my_k * a.ld_qkv + st * 16 + grp * 8);
+    } else {
+      float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      frag_from_f32(kf[st], z);
+      frag_from_f32(vf[st], z);
+    }
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dk[dt][r] = 0.f; dv[dt][r] = 0.f; }
+
+  const int qs = CAUSAL ? (k0 / BQ) * BQ : 0;
+  const int ntiles = s > qs ? (s - qs + BQ - 1) / BQ : 0;
+  RT q_ld, d_ld;
+  TT qt_ld, dt_ld;
+  auto load_tile = [&](int q0) {
+    q_ld.load(Qg, a.ld_qkv, q0, s, tid);
+    d_ld.load(dOg, a.ld_ctx, q0, s, tid);
+    qt_ld.load(Qg, a.ld_qkv, q0, s, tid);
+    dt_ld.load(dOg, a.ld_ctx, q0, s, tid);
+  };
+  auto store_tile = [&](int buf, int q0) {
+    q_ld.store(sQ[buf], tid);
+    d_ld.store(sdO[buf], tid);
+    qt_ld.store(sQt[buf], tid);
+    dt_ld.store(sdOt[buf], tid);
+    if (tid < BQ) {
+      const int q = q0 + tid;
+      sL[buf][tid] = q < s ? a.lse[stat + q] * kLog2e : 0.f;
+      sDl[buf][tid] = q < s ? a.delta[stat + q] : 0.f;
+    }
+  };
+  if (ntiles > 0) {
+    load_tile(qs);
+    store_tile(0, qs);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1, q0 = qs + t * BQ;
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(q0 + BQ);
+    if (!CAUSAL || q0 + BQ - 1 >= k0w) {
+      f32x16 sc[2], dp[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { sc[qt][r] = 0.f; dp[qt][r] = 0.f; }
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+          Frag8<T> qf, df;
+          load_frag(qf, &sQ[cur][(qt * 32 + l32) * RT::kLd + st * 16 + grp * 8]);
+          load_frag(df, &sdO[cur][(qt * 32 + l32) * RT::kLd + st * 16 + grp * 8]);
+          mfma_step(sc[qt], qf, kf[st]);   // S[q][key], lane owns key
+          mfma_step(dp[qt], df, vf[st]);   // dP[q][key]
+        }
+      }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int qo = qt * 32 + 8 * rq + 4 * grp;
+          const f32x4 lq = *reinterpret_cast<const f32x4*>(&sL[cur][qo]);
+          const f32x4 dq = *reinterpret_cast<const f32x4*>(&sDl[cur][qo]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rq + e, q = q0 + qo + e;
+            const bool ok = q < s && my_k < s && (!CAUSAL || my_k <= q);
+            const float p = ok ? exp2f(sc[qt][r] * c - lq[e]) : 0.f;
+            sc[qt][r] = p;                          // P
+            dp[qt][r] = p * (dp[qt][r] - dq[e]);    // dS
+          }
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        Frag8<T> pf, sf;
+        acc_frag(pf, sc[ks >> 1], 8 * (ks & 1));
+        acc_frag(sf, dp[ks >> 1], 8 * (ks & 1));
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          Frag8<T> of, qf;
+          load_frag(of, &sdOt[cur][(dt * 32 + l32) * TT::kLd + ks * 16 + grp * 8]);
+          load_frag(qf, &sQt[cur][(dt * 32 + l32) * TT::kLd + ks * 16 + grp * 8]);
+          mfma_step(dv[dt], of, pf);
+          mfma_step(dk[dt], qf, sf);
+        }
+      }
+    }
+    if (more) store_tile(cur ^ 1, q0 + BQ);
+    __syncthreads();
+  }
+  if (my_k < s) {
+    T* dKg = reinterpret_cast<T*>(a.dqkv) + (int64_t)b * s * a.ld_qkv + hr + hd * D;
+    store_rows<T, D>(dKg, a.ld_qkv, my_k, dk, rsqrtf((float)D), grp);
+    store_rows<T, D>(dKg + hr, a.ld_qkv, my_k, dv, 1.f, grp);
+  }
+}
+
+// Visible query-key pairs over all heads and sequences (causal: s(s+1)/2 each).
+double attn_pairs(const AttnDesc& d) {
+  const double s = d.seq;
+  return (double)d.batch * d.heads * (d.causal ? s * (s + 1) / 2 : s * s);
+}
+
+Args make_args(const AttnDesc& d) {
+  Args a;
+  a.qkv = static_cast<const char*>(d.qkv); a.ld_qkv = d.ld_qkv;
+  a.ctx = static_cast<char*>(d.ctx); a.ld_ctx = d.ld_ctx;
+  a.lse = d.lse;
+  a.dctx = static_cast<const char*>(d.dctx);
+  a.dqkv = static_cast<char*>(d.dqkv);
+  a.delta = d.delta;
+  a.batch = d.batch; a.heads = d.heads; a.seq = d.seq;
+  return a;
+}
+
+template <typename T, int D>
+hipError_t fwd_t(const AttnDesc& d, hipStream_t s) {
+  Args a = make_args(d);
+  dim3 grid((d.seq + 127) / 128, d.batch * d.heads);
+  if (d.causal) hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t bwd_t(const AttnDesc& d, hipStream_t s) {
+  Args a = make_args(d);
+  {
+    TraceScope trace(K_ATTN_BWD_PRE, s, (double)d.batch * d.seq * d.heads * d.head_dim * 2 * dtype_size(d.dtype));
+    const int64_t total = (int64_t)d.batch * d.heads * d.seq;
+    hipLaunchKernelGGL((attn_bwd_pre_kernel<T, D>), dim3((total + 255) / 256), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((d.seq + 127) / 128, d.batch * d.heads);
+  {
+    TraceScope trace(K_ATTN_BWD_DKDV, s, 6.0 * attn_pairs(d) * d.head_dim);   // dV, dP, dK
+    if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false>), grid, dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  TraceScope trace(K_ATTN_BWD_DQ, s, 2.0 * attn_pairs(d) * d.head_dim);     // dQ
+  if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// bf16: head_dim 64, 96, 128. fp32: head_dim 64 only (the fp32 backward's LDS
+// tiles for larger heads exceed the 160 KB of a workgroup).
+hipError_t launch_attn_fwd(const AttnDesc& d, hipStream_t s) {
+  TraceScope trace(K_ATTN_FWD, s, 4.0 * attn_pairs(d) * d.head_dim);       // QK^T, PV
+  if (d.dtype == DT_F32) return d.head_dim == 64 ? fwd_t<float, 64>(d, s) : hipErrorInvalidValue;
+  switch (d.head_dim) {
+    case 64: return fwd_t<bf16, 64>(d, s);
+    case 96: return fwd_t<bf16, 96>(d, s);
+    case 128: return fwd_t<bf16, 128>(d, s);
+  }
+  return hipErrorInvalidValue;
+}
+hipError_t launch_attn_bwd(const AttnDesc& d, hipStream_t s) {
+  if (d.dtype == DT_F32) return d.head_dim == 64 ? bwd_t<float, 64>(d, s) : hipErrorInvalidValue;
+  switch (d.head_dim) {
+    case 64: return bwd_t<bf16, 64>(d, s);
+    case 96: return bwd_t<bf16, 96>(d, s);
+    case 128: return bwd_t<bf16, 128>(d, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tpl

@@ -1,0 +1,91 @@
+// Internal launchers of the gfx950 kernels (host-callable, enqueue only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpl {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+inline size_t dtype_size(int dt) { return dt == DT_BF16 ? 2 : 4; }
+
+// ------------------------------------------------------------------ tracing
+// Optional per-launch event timing (see tpl_trace_enable in tp_layer.h).
+enum KernelId {
+  K_GEMM_NT = 0, K_GEMM_NN, K_GEMM_TN, K_ATTN_FWD, K_ATTN_BWD_PRE, K_ATTN_BWD_DQ,
+  K_ATTN_BWD_DKDV, K_LN_FWD, K_LN_BWD, K_LN_BWD_COLS, K_COLSUM, K_COLSUM_FINAL,
+  K_PARTIAL_SUM, K_XENT_STATS, K_XENT_FINISH, K_XENT_DLOGITS, K_COUNT
+};
+const char* kernel_name(int id);
+struct TraceScope {
+  int slot;
+  hipStream_t stream;
+  TraceScope(int kernel_id, hipStream_t s, double work = 0.0);
+  ~TraceScope();
+};
+
+// ------------------------------------------------------------------ GEMM
+// C[M][N] = sum_k A(m,k) B(n,k) with an epilogue.
+enum Epilogue {
+  EPI_NONE = 0,       // C = acc
+  EPI_BIAS = 1,       // C = acc + bias[n]
+  EPI_BIAS_GELU = 2,  // C = u = acc + bias[n]; C2 = GeLU(u)
+  EPI_DGELU = 3       // C = acc * GeLU'(C2[m][n])  (C2 holds u, read-only)
+};
+struct GemmDesc {
+  int dtype;          // storage type of A, B (and C unless c_f32)
+  bool a_kmajor;      // A(m,k) at A[m*lda+k] (true) or A[k*lda+m] (false)
+  bool b_kmajor;      // B(n,k) at B[n*ldb+k] (true) or B[k*ldb+n] (false)
+  int epi;
+  bool c_f32;         // C is fp32 (weight gradients) instead of the storage type
+  int64_t M, N, K;
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  void* C; int64_t ldc;
+  void* C2; int64_t ldc2;
+  const void* bias;
+};
+hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+struct AttnDesc {
+  int dtype, batch, heads, seq, head_dim, causal;
+  const void* qkv; int64_t ld_qkv;  // [N][3*h_r]: Q heads | K heads | V heads
+  void* ctx; int64_t ld_ctx;        // [N][h_r]
+  float* lse;                       // [batch][heads][seq]
+  // backward
+  const void* dctx;                 // [N][h_r]
+  void* dqkv;                       // [N][3*h_r]
+  float* delta;                     // [batch][heads][seq]
+};
+hipError_t launch_attn_fwd(const AttnDesc& d, hipStream_t s);
+hipError_t launch_attn_bwd(const AttnDesc& d, hipStream_t s);
+
+// ------------------------------------------------------------------ row / column ops
+hipError_t launch_layernorm_fwd(int dtype, const void* x, const void* g, const void* b, void* y,
+                                float* mu, float* rstd, int64_t rows, int cols, float eps,
+                                hipStream_t s);
+// dx = dy + LN_bwd(dsum); column partials of (dsum*xhat, dsum, dy) into ws.
+hipError_t launch_layernorm_bwd(int dtype, const void* dy, const void* dsum, const void* x,
+                                const float* mu, const float* rstd, const void* g, void* dx,
+                                float* d_g, float* d_b, float* d_bout, float* ws, int64_t rows,
+                                int cols, hipStream_t s);
+size_t layernorm_bwd_ws_floats(int64_t rows, int cols);
+// out[c] = sum_r X[r][c] over rows (two deterministic stages, ws partials).
+hipError_t launch_colsum(int dtype, const void* X, int64_t ld, int64_t rows, int cols, float* out,
+                         float* ws, hipStream_t s);
+size_t colsum_ws_floats(int64_t rows, int cols);
+hipError_t launch_partial_sum(int dtype, const void* const* parts, int n, const void* bias,
+                              const void* residual, void* out, int64_t rows, int cols,
+                              hipStream_t s);
+
+// ------------------------------------------------------------------ cross-entropy
+hipError_t launch_xent_stats(int dtype, const void* logits, int64_t rows, int vr,
+                             const int32_t* targets, int64_t v0, float* stats, hipStream_t s);
+hipError_t launch_xent_finish(const float* const* all_stats, int t, int64_t rows,
+                              const uint8_t* mask, float* lse, float* loss_rows, float* loss,
+                              hipStream_t s);
+hipError_t launch_xent_dlogits(int dtype, void* logits, int64_t rows, int vr,
+                               const int32_t* targets, int64_t v0, const uint8_t* mask,
+                               const float* lse, const float* loss, float dloss, hipStream_t s);
+
+}  // namespace tpl

@@ -1,0 +1,166 @@
+// Vocabulary-parallel cross-entropy (guide page section 3.3; podcast page
+// Outline: the output embedding is split along the vocabulary and the gather
+// is deferred into the loss). Each rank reduces its logits shard to three
+// numbers per row -- running max m, sum of exp(l - m), target logit (or 0) --
+// so the softmax over the shard is never written; ranks then exchange only
+// these [N, 3] statistics, combined by log-sum-exp rescaling.
+#include "common.h"
+#include "kernels.h"
+
+namespace tpl {
+namespace {
+
+// Merge (m, s) pairs of the online log-sum-exp.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+  m = mn;
+}
+
+// One workgroup per row: stats[row] = (max, sum exp(l - max), target logit or 0).
+template <typename T>
+__global__ __launch_bounds__(256) void xent_stats_kernel(const T* __restrict__ logits, int vr,
+                                                         const int32_t* __restrict__ targets, int64_t v0,
+                                                         float* __restrict__ stats) {
+  constexpr int V = Vec16<T>::N;
+  const int64_t row = blockIdx.x;
+  const T* lr = logits + row * vr;
+  float m = -INFINITY, s = 0.f;
+  for (int ch = threadIdx.x; ch < vr / V; ch += 256) {
+    Vec16<T> x;
+    x.raw = ld16(lr + ch * V);
+    float v[V], mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < V; ++e) { v[e] = to_f32(x.get(e)); mx = fmaxf(mx, v[e]); }
+    const float mn = fmaxf(m, mx);
+    float acc = s * __expf(m - mn);
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc += __expf(v[e] - mn);
+    m = mn;
+    s = acc;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(s, o, kWave);
+    lse_merge(m, s, m2, s2);
+  }
+  __shared__ float sm[4], ss[4];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sm[wave] = m; ss[wave] = s; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = sm[0], S = ss[0];
+    for (int w = 1; w < 4; ++w) lse_merge(M, S, sm[w], ss[w]);
+    const int64_t t = (int64_t)targets[row] - v0;
+    const float tl = (t >= 0 && t < vr) ? to_f32(lr[t]) : 0.f;
+    stats[row * 3 + 0] = M;
+    stats[row * 3 + 1] = S;
+    stats[row * 3 + 2] = tl;
+  }
+}
+
+struct StatPtrs { const float* p[64]; };
+
+// Single workgroup: combine the t ranks' statistics, per-row loss and the
+// masked mean (fixed reduction order -> deterministic).
+__global__ __launch_bounds__(1024) void xent_finish_kernel(StatPtrs st, int t, int64_t rows,
+                                                           const uint8_t* __restrict__ mask,
+                                                           float* __restrict__ lse, float* __restrict__ loss_rows,
+                                                           float* __restrict__ loss) {
+  float acc = 0.f, cnt = 0.f;
+  for (int64_t r = threadIdx.x; r < rows; r += 1024) {
+    float M = -INFINITY;
+    for (int k = 0; k < t; ++k) M = fmaxf(M, st.p[k][r * 3]);
+    float S = 0.f, TL = 0.f;
+    for (int k = 0; k < t; ++k) {
+      S += st.p[k][r * 3 + 1] * __expf(st.p[k][r * 3] - M);
+      TL += st.p[k][r * 3 + 2];
+    }
+    const float l = M + __logf(S);
+    const float w = mask ? (float)mask[r] : 1.f;
+    const float lr = w * (l - TL);
+    lse[r] = l;
+    loss_rows[r] = lr;
+    acc += lr;
+    cnt += w;
+  }
+  __shared__ float sa[16], sc[16];
+  acc = wave_sum(acc);
+  cnt = wave_sum(cnt);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sa[wave] = acc; sc[wave] = cnt; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float A = 0.f, C = 0.f;
+    for (int w = 0; w < 16; ++w) { A += sa[w]; C += sc[w]; }
+    loss[0] = C > 0.f ? A / C : 0.f;
+    loss[1] = C;
+  }
+}
+
+// In place: l <- g (exp(l - lse) - [j == target - v0]), g = dloss * mask / count.
+template <typename T>
+__global__ __launch_bounds__(256) void xent_dlogits_kernel(T* logits, int vr, const int32_t* __restrict__ targets,
+                                                           int64_t v0, const uint8_t* __restrict__ mask,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ loss, float dloss) {
+  constexpr int V = Vec16<T>::N;
+  const int64_t row = blockIdx.x;
+  T* lr = logits + row * vr;
+  const float cnt = loss[1];
+  const float g = (mask ? (float)mask[row] : 1.f) * (cnt > 0.f ? dloss / cnt : 0.f);
+  const float L = lse[row];
+  const int64_t t = (int64_t)targets[row] - v0;
+  for (int ch = threadIdx.x; ch < vr / V; ch += 256) {
+    Vec16<T> x;
+    x.raw = ld16(lr + ch * V);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int j = ch * V + e;
+      float p = __expf(to_f32(x.get(e)) - L);
+      if (j == t) p -= 1.f;
+      x.set(e, from_f32<T>(g * p));
+    }
+    st16(lr + ch * V, x.raw);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_xent_stats(int dtype, const void* logits, int64_t rows, int vr, const int32_t* targets,
+                             int64_t v0, float* stats, hipStream_t s) {
+  TraceScope trace(K_XENT_STATS, s, (double)rows * vr * dtype_size(dtype) + rows * 16.0);
+  if (rows == 0) return hipSuccess;
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(xent_stats_kernel<bf16>, dim3((unsigned)rows), dim3(256), 0, s,
+                       static_cast<const bf16*>(logits), vr, targets, v0, stats);
+  else
+    hipLaunchKernelGGL(xent_stats_kernel<float>, dim3((unsigned)rows), dim3(256), 0, s,
+                       static_cast<const float*>(logits), vr, targets, v0, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_xent_finish(const float* const* all_stats, int t, int64_t rows, const uint8_t* mask, float* lse,
+                              float* loss_rows, float* loss, hipStream_t s) {
+  TraceScope trace(K_XENT_FINISH, s, (double)rows * (12.0 * t + 9));
+  StatPtrs sp;
+  for (int i = 0; i < 64; ++i) sp.p[i] = i < t ? all_stats[i] : nullptr;
+  hipLaunchKernelGGL(xent_finish_kernel, dim3(1), dim3(1024), 0, s, sp, t, rows, mask, lse, loss_rows, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_xent_dlogits(int dtype, void* logits, int64_t rows, int vr, const int32_t* targets, int64_t v0,
+                               const uint8_t* mask, const float* lse, const float* loss, float dloss, hipStream_t s) {
+  TraceScope trace(K_XENT_DLOGITS, s, (double)rows * vr * 2 * dtype_size(dtype) + rows * 9.0);
+  if (rows == 0) return hipSuccess;
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(xent_dlogits_kernel<bf16>, dim3((unsigned)rows), dim3(256), 0, s, static_cast<bf16*>(logits),
+                       vr, targets, v0, mask, lse, loss, dloss);
+  else
+    hipLaunchKernelGGL(xent_dlogits_kernel<float>, dim3((unsigned)rows), dim3(256), 0, s,
+                       static_cast<float*>(logits), vr, targets, v0, mask, lse, loss, dloss);
+  return hipGetLastError();
+}
+
+}  // namespace tpl

@@ -1,0 +1,49 @@
+"""Parity of the MFMA GEMM (every operand layout, both storage types, ragged
+and multi-tile shapes) against the oracle's dense product (GPU)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tensor_transformer_layer_03_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+# (dtype, a_kmajor, b_kmajor, M, N, K, bias)
+CASES = [
+    ("bf16", 1, 1, 300, 264, 136, True), ("bf16", 1, 0, 300, 264, 136, False), ("bf16", 0, 0, 264, 136, 300, False),
+    ("f32", 1, 1, 300, 264, 136, True), ("f32", 1, 0, 300, 264, 136, False), ("f32", 0, 0, 264, 136, 300, False),
+    ("bf16", 1, 1, 1024, 1024, 1024, False), ("bf16", 1, 1, 2048, 768, 520, True),
+    ("bf16", 1, 0, 4096, 1024, 512, False), ("bf16", 0, 0, 1024, 512, 4000, False),
+    ("bf16", 1, 1, 1, 8, 8, False), ("bf16", 0, 0, 8, 8, 1, False),
+]
+
+
+def _dev(a, dtype):
+    a = np.ascontiguousarray(a, np.float32)
+    if dtype == "bf16":
+        return torch.from_numpy(synth.bf16_bits(a)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_gemm(case):
+    dtype, ak, bk, M, N, K, use_bias = case
+    g = np.random.default_rng(M * 7 + N * 3 + K)
+    rnd = (lambda a: synth.round_to_bf16(a)) if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    A = rnd(g.standard_normal((M, K)).astype(np.float32))    # logical A[m][k]
+    Bm = rnd(g.standard_normal((N, K)).astype(np.float32))   # logical B[n][k]
+    bias = rnd(g.standard_normal(N).astype(np.float32)) if use_bias else None
+    dA = _dev(A if ak else A.T, dtype)
+    dB = _dev(Bm if bk else Bm.T, dtype)
+    c_f32 = (not ak) and (not bk)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32 if c_f32 else dA.dtype, device="cuda")
+    B.tpl_gemm(B.TPL_BF16 if dtype == "bf16" else B.TPL_F32, ak, bk, M, N, K, dA, K if ak else M, dB,
+               K if bk else N, None if bias is None else _dev(bias, dtype), C, N, c_f32)
+    torch.cuda.synchronize()
+    ref = O.linear(A, Bm, bias)
+    got = C.float().cpu().numpy()
+    rep = O.compare.compare_tensor(got, ref, "f32" if c_f32 or dtype == "f32" else "bf16")
+    print(case, rep)
+    assert rep["ok"], rep
