@@ -23,6 +23,9 @@
 //  * workgroups are renumbered so that consecutive tiles share an XCD (the
 //    dispatcher deals workgroups to the 8 XCDs round-robin, each with its own
 //    L2), then walked in groups of GROUP_M tile-rows for L2 reuse of B.
+#include <cstdlib>
+#include <cstring>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -257,9 +260,300 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave) void gemm_kernel(Args g)
   }
 }
 
+// ------------------------------------------------------------------ bf16 kernel
+// Direct-to-LDS version for bf16: every operand tile goes global -> LDS with
+// buffer_load_dwordx4 ... lds (lane l of a wave writes bytes 16l..16l+15 of a
+// 1 KB LDS block; the swizzle is produced by choosing which 16 B each lane
+// fetches), so no registers or VALU are spent on staging. Reads past the end
+// of an operand (num_records of the buffer resource) return zeros.
+//  K-major tile  [rows][64 k]: 128 B rows, chunk c of row r at c ^ swz_k(r);
+//    a fragment (8 consecutive k of one row) is one ds_read_b128.
+//  MN-major tile [64 k][rows]: rows of 2*ROWS bytes, chunk c of row k at
+//    c ^ 2*(k & 3); a fragment is two ds_read_b64_tr_b16: within each group of
+//    16 lanes the instruction hands lane j element j%4 of the 8 bytes read by
+//    lanes j/4, j/4+4, j/4+8, j/4+12, so source lane 4e+q points at row k0+e,
+//    columns base+4q..base+4q+3 and lane j receives column base+j, rows
+//    k0..k0+3 -- four consecutive k of one output row/column, as the MFMA wants.
+//
+// Schedule of one K-tile (4 k16-steps, one barrier): the loads of tile kt+1
+// are issued during step 0, interleaved with its MFMAs; the fragments of step
+// s+1 are read during the MFMAs of step s; the barrier sits inside step 3
+// (after the wave's loads of tile kt+1 have landed), and the first fragments
+// of tile kt+1 are read while the rest of step 3's MFMAs run. The body is one
+// basic block: past the last tile the loads go to a zero-length buffer.
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((__vector_size__(8)));
+
+// Row swizzle of K-major tiles; depends on r mod 32 only, so the 32-row
+// fragments of a wave share one lane pattern.
+__device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 3); }
+__device__ __forceinline__ int swz_t(int k) { return 2 * (k & 3); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
+  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, n, 0x00020000);
+}
+
+// Direct-to-LDS loads of one operand tile (ROWS x 64 bf16) for one wave:
+// kInst instructions of 1 KB; per-lane byte offsets are fixed over K.
+template <int ROWS, bool KMAJ, int NW>
+struct TileDma {
+  static constexpr bool kKMajor = KMAJ;
+  static constexpr int kRows = ROWS;
+  static constexpr int kInst = ROWS * 128 / 1024 / NW;
+  static_assert(kInst * 1024 * NW == ROWS * 128, "tile does not split evenly over the waves");
+  int voff[kInst];
+  __device__ __forceinline__ void init(int64_t ld, int row0, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < kInst; ++j) {
+      const int blk = j * NW + wave;
+      if constexpr (KMAJ) {
+        const int r = blk * 8 + (lane >> 3);
+        voff[j] = (int)(((int64_t)r * ld + (((lane & 7) ^ swz_k(r)) * 8)) * 2);
+      } else {
+        constexpr int kChunks = ROWS / 8, kRowsPerBlk = 64 / kChunks;
+        const int k = blk * kRowsPerBlk + lane / kChunks;
+        voff[j] = (int)(((int64_t)k * ld + row0 + (((lane % kChunks) ^ swz_t(k)) * 8)) * 2);
+      }
+    }
+  }
+  // Loads from a buffer starting at `base` of `bytes` bytes (0: nothing is read,
+  // zeros are written). K-major: base = the block's first row, soff = 2*k0.
+  // MN-major: base = k-row k0, soff = 0.
+  __device__ __forceinline__ void issue(const char* base, int64_t bytes, int soff, char* lds, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)   // the buffer-resource type exists only in the device pass
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+#pragma unroll
+    for (int j = 0; j < kInst; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (j * NW + wave) * 1024), 16, voff[j], soff, 0, 0);
+#endif
+  }
+};
+
+// Loads of K-tile KT_ of both operands into stage S_; past the last tile the
+// buffers are zero-length (nothing is read, zeros are written).
+#define TPL_ISSUE_TILES(KT_, S_)                                                                                   \
+  do {                                                                                                             \
+    const int kt_ = (KT_);                                                                                         \
+    char* s_ = (S_);                                                                                               \
+    const bool live_ = kt_ * 64 < g.K;                                                                             \
+    if constexpr (A_K)                                                                                             \
+      dA.issue(g.A + (int64_t)m0 * g.lda * 2, live_ ? (int64_t)(g.M - m0) * g.lda * 2 : 0, kt_ * 128, s_, wave);  \
+    else                                                                                                           \
+      dA.issue(g.A + (int64_t)kt_ * 64 * g.lda * 2, live_ ? (int64_t)(g.K - kt_ * 64) * g.lda * 2 : 0, 0, s_,      \
+               wave);                                                                                              \
+    if constexpr (B_K)                                                                                             \
+      dB.issue(g.B + (int64_t)n0 * g.ldb * 2, live_ ? (int64_t)(g.N - n0) * g.ldb * 2 : 0, kt_ * 128,             \
+               s_ + BM * 128, wave);                                                                               \
+    else                                                                                                           \
+      dB.issue(g.B + (int64_t)kt_ * 64 * g.ldb * 2, live_ ? (int64_t)(g.K - kt_ * 64) * g.ldb * 2 : 0, 0,          \
+               s_ + BM * 128, wave);                                                                               \
+  } while (0)
+
+// Fragment of tile row r0 + lane%32, k-slots 8*(lane/32)..+7 of step st.
+template <int ROWS, bool KMAJ>
+__device__ __forceinline__ void frag_v2(Frag8<bf16>& f, const char* tile, int r0, int st, int lane) {
+  if constexpr (KMAJ) {
+    const int r = r0 + (lane & 31);
+    const int c = (2 * st + (lane >> 5)) ^ swz_k(r);
+    load_frag(f, reinterpret_cast<const bf16*>(tile + r * 128 + c * 16));
+  } else {
+    const int G = lane >> 4, s = lane & 15, e = s >> 2, q = s & 3;
+    const int mn = r0 + 16 * (G & 1) + 4 * q;
+    const int k = 16 * st + 8 * (G >> 1) + e;
+    const int c0 = (mn >> 3) ^ swz_t(k);   // swz_t(k) == swz_t(k + 4)
+    const char* p0 = tile + k * (ROWS * 2) + c0 * 16 + (q & 1) * 8;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+    const s16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 4 * ROWS * 2));
+    __builtin_memcpy(reinterpret_cast<char*>(&f.v), &lo, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&f.v) + 8, &hi, 8);
+  }
+}
+
+// Fragments of step st for a wave's TM row tiles (A) and TN column tiles (B).
+template <int BM, int BN, bool A_K, bool B_K, int TM, int TN>
+__device__ __forceinline__ void read_frags(Frag8<bf16> (&fa)[TM], Frag8<bf16> (&fb)[TN], const char* stage, int st,
+                                           int arow, int brow, int lane) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i) frag_v2<BM, A_K>(fa[i], stage, arow + i * 32, st, lane);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) frag_v2<BN, B_K>(fb[j], stage + BM * 128, brow + j * 32, st, lane);
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void mfma_tile(f32x16 (&acc)[TM][TN], const Frag8<bf16> (&fa)[TM],
+                                          const Frag8<bf16> (&fb)[TN]) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) mfma_step(acc[i][j], fb[j], fa[i]);
+}
+
+__device__ __forceinline__ void zero_frag(Frag8<bf16>& f) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  __builtin_memcpy(&f.v, &z, 16);
+}
+
+// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt low bits 3:0, high
+// bits 15:14; expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
+
+template <int BM, int BN, int WGM, int WGN, bool A_K, bool B_K, int EPI, typename TC>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN, TM = WTM / 32, TN = WTN / 32;
+  constexpr int kStage = (BM + BN) * 128;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % WGM, wn = wave / WGM;
+
+  const int nblk = g.tiles_m * g.tiles_n;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = nblk >> 3, rem = nblk & 7;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
+  const int in_group = kGroupM * g.tiles_n;
+  const int first_m = (logical / in_group) * kGroupM;
+  const int gsize = min(g.tiles_m - first_m, kGroupM);
+  const int m0 = (first_m + (logical % in_group) % gsize) * BM;
+  const int n0 = ((logical % in_group) / gsize) * BN;
+
+  TileDma<BM, A_K, WGM * WGN> dA;
+  TileDma<BN, B_K, WGM * WGN> dB;
+  dA.init(g.lda, A_K ? 0 : m0, wave, lane);
+  dB.init(g.ldb, B_K ? 0 : n0, wave, lane);
+
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  Frag8<bf16> fa[2][TM], fb[2][TN];
+  constexpr int kMf = TM * TN;                                // MFMAs per step
+  constexpr int kRd = (TM + TN) * (A_K && B_K ? 1 : 2);        // LDS read instructions per step (upper bound)
+  constexpr int kDma = TileDma<BM, A_K, WGM * WGN>::kInst + TileDma<BN, B_K, WGM * WGN>::kInst;
+
+  const int KT = g.K / 64;                  // full K-tiles; a partial last tile is handled after the loop
+  const int ktail = g.K & 63;
+  const int kt_all = KT + (ktail ? 1 : 0);
+
+  TPL_ISSUE_TILES(0, smem);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  read_frags<BM, BN, A_K, B_K, TM, TN>(fa[0], fb[0], smem, 0, wm * WTM, wn * WTN, lane);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const char* cur = smem + (kt & 1) * kStage;
+    char* nxt = smem + ((kt + 1) & 1) * kStage;
+    // step 0: loads of the next tile + fragments of step 1, around 16 MFMAs
+    TPL_ISSUE_TILES(kt + 1, nxt);
+    read_frags<BM, BN, A_K, B_K, TM, TN>(fa[1], fb[1], cur, 1, wm * WTM, wn * WTN, lane);
+    mfma_tile<TM, TN>(acc, fa[0], fb[0]);
+#pragma unroll
+    for (int x = 0; x < kMf; ++x) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (x < kDma) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+      if (x < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
+    // steps 1, 2
+    read_frags<BM, BN, A_K, B_K, TM, TN>(fa[0], fb[0], cur, 2, wm * WTM, wn * WTN, lane);
+    mfma_tile<TM, TN>(acc, fa[1], fb[1]);
+#pragma unroll
+    for (int x = 0; x < kMf; ++x) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (x < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
+    read_frags<BM, BN, A_K, B_K, TM, TN>(fa[1], fb[1], cur, 3, wm * WTM, wn * WTN, lane);
+    mfma_tile<TM, TN>(acc, fa[0], fb[0]);
+#pragma unroll
+    for (int x = 0; x < kMf; ++x) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (x < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
+    // step 3: a few MFMAs, then sync on the next tile, then its first fragments
+    // are read while the remaining MFMAs of this step run
+    constexpr int kHead = kMf / 4;
+#pragma unroll
+    for (int x = 0; x < kHead; ++x) mfma_step(acc[x / TN][x % TN], fb[1][x % TN], fa[1][x / TN]);
+    __builtin_amdgcn_s_waitcnt(0);          // this wave's loads of tile kt+1 have landed, its reads are done
+    __builtin_amdgcn_s_barrier();            // ... and every other wave's
+    read_frags<BM, BN, A_K, B_K, TM, TN>(fa[0], fb[0], nxt, 0, wm * WTM, wn * WTN, lane);
+#pragma unroll
+    for (int x = kHead; x < kMf; ++x) mfma_step(acc[x / TN][x % TN], fb[1][x % TN], fa[1][x / TN]);
+#pragma unroll
+    for (int x = kHead; x < kMf; ++x) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (x - kHead < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
+  }
+  if (ktail) {
+    // partial last tile (its loads were issued by the last loop iteration, or
+    // by the prologue when K < 64): k-slots at or past K contribute zero
+    const char* cur = smem + (KT & 1) * kStage;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if (st > 0) read_frags<BM, BN, A_K, B_K, TM, TN>(fa[0], fb[0], cur, st, wm * WTM, wn * WTN, lane);
+      if (KT * 64 + 16 * st + 8 * (lane >> 5) >= g.K) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) zero_frag(fa[0][i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) zero_frag(fb[0][j]);
+      }
+      mfma_tile<TM, TN>(acc, fa[0], fb[0]);
+    }
+  }
+  (void)kt_all;
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (n >= g.N) continue;
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
+          float b[4];
+          load4(reinterpret_cast<const bf16*>(g.bias) + n, b);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += b[e];
+        }
+        if constexpr (EPI == EPI_DGELU) {
+          float u[4];
+          load4(reinterpret_cast<const bf16*>(g.C2) + (int64_t)m * g.ldc2 + n, u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
+        }
+        store4(reinterpret_cast<TC*>(g.C) + (int64_t)m * g.ldc + n, v[0], v[1], v[2], v[3]);
+        if constexpr (EPI == EPI_BIAS_GELU) {
+          bf16* ap = reinterpret_cast<bf16*>(g.C2) + (int64_t)m * g.ldc2 + n;
+          store4(ap, gelu_f(v[0]), gelu_f(v[1]), gelu_f(v[2]), gelu_f(v[3]));
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ dispatch
 
-struct TileCfg { int bm, bn; };
+struct TileCfg { int bm, bn, variant; };
 
 template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BK_, int EPI, typename TC>
 hipError_t run(const GemmDesc& d, hipStream_t s) {
@@ -279,31 +573,62 @@ hipError_t run(const GemmDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Pick the tile that minimises (rounds of workgroups over 256 CUs) x (tile cost).
-TileCfg choose_tile(int dtype, int64_t M, int64_t N) {
-  if (dtype == DT_F32) return {128, 128};
-  struct Cand { int bm, bn, per_cu; double eff; };
-  const Cand cands[] = {{256, 256, 1, 1.00}, {256, 128, 1, 0.90}, {128, 128, 2, 0.78}};
-  double best = 1e300;
-  TileCfg pick{128, 128};
-  for (const Cand& c : cands) {
-    int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    int64_t rounds = (tiles + 256 * c.per_cu - 1) / (256 * c.per_cu);
-    double cost = (double)rounds * c.bm * c.bn / c.eff / c.per_cu;
-    if (cost < best * 0.999) { best = cost; pick = {c.bm, c.bn}; }
+// Tile choice (measured on MI355X over the layer's shapes): the 256x256 tile
+// with 8 waves when it yields at least 384 workgroups (1.5 rounds over the
+// 256 CUs), otherwise 128x128 (two workgroups per CU); products with both
+// operands MN-major (weight gradients) use 128x128. TPL_GEMM_TILE=
+// 256x256[w8[t]] | 256x128[w8[t]] | 128x128 forces a shape (the tests use it
+// to cover every tile path).
+TileCfg choose_tile(int dtype, bool a_kmajor, bool b_kmajor, int64_t M, int64_t N) {
+  if (dtype == DT_F32) return {128, 128, 0};
+  if (const char* f = getenv("TPL_GEMM_TILE")) {
+    if (!strcmp(f, "256x256")) return {256, 256, 0};
+    if (!strcmp(f, "256x256w8")) return {256, 256, 1};
+    if (!strcmp(f, "256x256w8t")) return {256, 256, 2};
+    if (!strcmp(f, "256x128")) return {256, 128, 0};
+    if (!strcmp(f, "256x128w8")) return {256, 128, 3};
+    if (!strcmp(f, "256x128w8t")) return {256, 128, 4};
+    if (!strcmp(f, "128x128")) return {128, 128, 0};
   }
-  return pick;
+  if (!a_kmajor && !b_kmajor) return {128, 128, 0};
+  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big >= 384) return {256, 256, 1};
+  return {128, 128, 0};
+}
+
+template <int BM, int BN, int WGM, int WGN, bool AK, bool BK_, int EPI, typename TC>
+hipError_t run_v2(const GemmDesc& d, hipStream_t s) {
+  Args a;
+  a.A = static_cast<const char*>(d.A); a.lda = d.lda;
+  a.B = static_cast<const char*>(d.B); a.ldb = d.ldb;
+  a.C = static_cast<char*>(d.C); a.ldc = d.ldc;
+  a.C2 = static_cast<char*>(d.C2); a.ldc2 = d.ldc2;
+  a.bias = static_cast<const char*>(d.bias);
+  a.M = (int)d.M; a.N = (int)d.N; a.K = (int)d.K;
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.tiles_n = (a.N + BN - 1) / BN;
+  const int nblk = a.tiles_m * a.tiles_n;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, AK, BK_, EPI, TC>), dim3(nblk), dim3(WGM * WGN * 64), 0, s, a);
+  return hipGetLastError();
 }
 
 template <typename T, bool AK, bool BK_, int EPI, typename TC>
 hipError_t run_tiles(const GemmDesc& d, hipStream_t s) {
-  TileCfg t = choose_tile(d.dtype, d.M, d.N);
   if constexpr (sizeof(T) == 4) {
     return run<T, 128, 128, 2, 2, AK, BK_, EPI, TC>(d, s);
   } else {
-    if (t.bm == 256 && t.bn == 256) return run<T, 256, 256, 2, 2, AK, BK_, EPI, TC>(d, s);
-    if (t.bm == 256 && t.bn == 128) return run<T, 256, 128, 2, 2, AK, BK_, EPI, TC>(d, s);
-    return run<T, 128, 128, 2, 2, AK, BK_, EPI, TC>(d, s);
+    const TileCfg t = choose_tile(d.dtype, d.a_kmajor, d.b_kmajor, d.M, d.N);
+    switch (t.variant) {
+      case 1: return run_v2<256, 256, 2, 4, AK, BK_, EPI, TC>(d, s);
+      case 2: return run_v2<256, 256, 4, 2, AK, BK_, EPI, TC>(d, s);
+      case 3: return run_v2<256, 128, 2, 4, AK, BK_, EPI, TC>(d, s);
+      case 4: return run_v2<256, 128, 4, 2, AK, BK_, EPI, TC>(d, s);
+      default: break;
+    }
+    if (t.bm == 256 && t.bn == 256) return run_v2<256, 256, 2, 2, AK, BK_, EPI, TC>(d, s);
+    if (t.bm == 256 && t.bn == 128) return run_v2<256, 128, 2, 2, AK, BK_, EPI, TC>(d, s);
+    return run_v2<128, 128, 2, 2, AK, BK_, EPI, TC>(d, s);
   }
 }
 

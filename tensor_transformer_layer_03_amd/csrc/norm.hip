@@ -200,16 +200,32 @@ __global__ __launch_bounds__(64) void colsum_kernel(const T* __restrict__ X, int
   for (int e = 0; e < V; ++e) w[e] = a[e];
 }
 
-// out_k[c] = sum over chunks (in order) of ws[chunk][k][c], for k < nout.
+// out_k[c] = sum over chunks of ws[chunk][k][c], for k < nout. One block of
+// 4 waves per 64 columns: wave w sums chunks w, w+4, ... (lane = column), the
+// four wave sums are then added in wave order -- a fixed order, so the result
+// is deterministic.
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ ws, int nchunks, int cols,
                                                            int nout, float* o0, float* o1, float* o2) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
-  float* outs[3] = {o0, o1, o2};
+  __shared__ float part[3][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
   for (int k = 0; k < nout; ++k) {
-    float s = 0.f;
-    for (int i = 0; i < nchunks; ++i) s += ws[((int64_t)i * nout + k) * cols + c];
-    outs[k][c] = s;
+    float s0 = 0.f, s1 = 0.f;
+    if (c < cols) {
+      int i = wave;
+      for (; i + 4 < nchunks; i += 8) {
+        s0 += ws[((int64_t)i * nout + k) * cols + c];
+        s1 += ws[((int64_t)(i + 4) * nout + k) * cols + c];
+      }
+      if (i < nchunks) s0 += ws[((int64_t)i * nout + k) * cols + c];
+    }
+    part[k][wave][lane] = s0 + s1;
+  }
+  __syncthreads();
+  if (wave == 0 && c < cols) {
+    float* outs[3] = {o0, o1, o2};
+    for (int k = 0; k < nout; ++k)
+      outs[k][c] = (part[k][0][lane] + part[k][1][lane]) + (part[k][2][lane] + part[k][3][lane]);
   }
 }
 
@@ -328,7 +344,7 @@ hipError_t launch_layernorm_bwd(int dtype, const void* dy, const void* dsum, con
   }
   {
     TraceScope trace(K_COLSUM_FINAL, s);
-    hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, ws, (int)n_chunks(rows), cols,
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64), dim3(256), 0, s, ws, (int)n_chunks(rows), cols,
                        3, d_g, d_b, d_bout);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -350,7 +366,7 @@ hipError_t launch_colsum(int dtype, const void* X, int64_t ld, int64_t rows, int
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   TraceScope trace(K_COLSUM_FINAL, s);
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 255) / 256), dim3(256), 0, s, ws, (int)n_chunks(rows), cols, 1,
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64), dim3(256), 0, s, ws, (int)n_chunks(rows), cols, 1,
                      out, nullptr, nullptr);
   return hipGetLastError();
 }

@@ -47,3 +47,15 @@ def test_gemm(case):
     rep = O.compare.compare_tensor(got, ref, "f32" if c_f32 or dtype == "f32" else "bf16")
     print(case, rep)
     assert rep["ok"], rep
+
+
+TILE_CASES = [(lay, tile) for lay in ((1, 1), (1, 0), (0, 0))
+              for tile in ("256x256", "256x256w8", "256x256w8t", "256x128", "256x128w8", "256x128w8t", "128x128")]
+
+
+@pytest.mark.parametrize("lay,tile", TILE_CASES, ids=lambda c: str(c))
+def test_gemm_every_tile_shape(lay, tile, monkeypatch):
+    """Force each workgroup tile shape on a ragged multi-tile product."""
+    monkeypatch.setenv("TPL_GEMM_TILE", tile)
+    ak, bk = lay
+    test_gemm(("bf16", ak, bk, 520, 776, 328, ak and bk))
