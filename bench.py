@@ -84,8 +84,9 @@ def traced_kernels(st, steps, B, dtype):
     return agg
 
 
-def roofline(agg, dtype, traffic=None):
+def roofline(agg, dtype):
     name, (count, ms, work) = max(agg.items(), key=lambda kv: kv[1][1])
+    traffic = measured_traffic(name)
     if name in MFMA_KERNELS:
         achieved = work / (ms / 1e3) / 1e12
         peak = PEAK_TFLOPS[dtype]
@@ -99,9 +100,10 @@ def roofline(agg, dtype, traffic=None):
             "avg_launch_us": round(ms / count * 1e3, 2), "bytes_per_launch": work / count}
 
 
-def cpu_baseline(cfg, seqs: int) -> dict:
+def cpu_baseline(cfg, seqs: int, repeats: int = 3) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload:
-    the first `seqs` sequences of the micro-batch (every flop of those rows)."""
+    `seqs` sequences of the micro-batch (every flop of those rows), median of
+    `repeats` runs."""
     import dataclasses
     import numpy as np
     import oracle as O
@@ -121,15 +123,18 @@ def cpu_baseline(cfg, seqs: int) -> dict:
     peers = synth.peer_partials(small, n_peers) if n_peers else []
     pstats = [synth.peer_stats(small, r) for r in range(small.tp) if r not in ranks]
     prs = {r: synth.oracle_params(small, [s], rep) for r, s in shards.items()}
-    t0 = time.perf_counter()
-    O.step_reference(prs, rep.x, rep.dout, rep.targets, rep.mask, seq=small.seq, causal=small.causal,
-                     eps=small.ln_eps, tp=small.tp, vocab_r=small.vocab_r, peers=peers, peer_stats=pstats,
-                     use_mask=small.mask_rows is not None)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        O.step_reference(prs, rep.x, rep.dout, rep.targets, rep.mask, seq=small.seq, causal=small.causal,
+                         eps=small.ln_eps, tp=small.tp, vocab_r=small.vocab_r, peers=peers, peer_stats=pstats,
+                         use_mask=small.mask_rows is not None)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     fl = step_flops(small, len(ranks))["total"]
     return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle pass (numpy fp64) over {seqs} of {cfg.micro_batch} sequences "
-                      f"({fl / 1e9:.0f} GFLOP in {dt:.1f} s)"}
+            "sample": f"oracle pass (numpy fp64) over {seqs} of {cfg.micro_batch} sequences, median of "
+                      f"{repeats} runs ({fl / 1e9:.0f} GFLOP in {dt:.1f} s each)"}
 
 
 def copy_calibration(torch, mib=1024, reps=5):
@@ -143,6 +148,118 @@ def copy_calibration(torch, mib=1024, reps=5):
     print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "reps": reps}))
 
 
+# ---------------------------------------------------------------- profile summaries
+
+SOURCES = {"gemm": "gemm.hip", "attn": "attention.hip", "layernorm": "norm.hip", "colsum": "norm.hip",
+           "partial": "norm.hip", "xent": "xent.hip"}
+PROFILE_CMDS = {
+    "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_c2 -o c2 -- "
+             "python3 <repo>/bench.py --steps 5 --warmup 2 --cpu-seqs 0",
+    "pmc": "cd /tmp && rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <out>/pmc_<counter> -o bench "
+           "-- python3 <repo>/bench.py --steps 2 --warmup 1 --cpu-seqs 0 --trace-steps 1",
+    "copy": "cd /tmp && rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <out>/pmc_<counter> -o copy "
+            "-- python3 <repo>/bench.py --copy-calibration",
+}
+
+
+def kernel_family(name: str) -> str:
+    """Map a rocprofv3 kernel name (mangled or demangled) to the trace names."""
+    import re
+    if "gemm" in name:
+        m = re.search(r"gemm_\w*kernel<([^>]*)>", name)
+        if m:
+            flags = [t.strip() == "true" for t in m.group(1).split(",") if t.strip() in ("true", "false")]
+        else:
+            flags = [f == "1" for f in re.findall(r"Lb([01])E", name)]
+        ak, bk = (flags + [True, True])[:2]
+        return "gemm_nt" if ak and bk else ("gemm_nn" if ak else "gemm_tn")
+    table = [("attn_bwd_dkdv", "attn_bwd_dkdv"), ("attn_bwd_dq", "attn_bwd_dq"), ("attn_bwd_pre", "attn_bwd_pre"),
+             ("attn_fwd", "attn_fwd"), ("ln_bwd_cols", "layernorm_bwd_cols"), ("ln_bwd", "layernorm_bwd"),
+             ("ln_fwd", "layernorm_fwd"), ("colsum_final", "colsum_final"), ("colsum", "colsum"),
+             ("partial_sum", "partial_sum"), ("xent_stats", "xent_stats"), ("xent_finish", "xent_finish"),
+             ("xent_dlogits", "xent_dlogits")]
+    for key, fam in table:
+        if key in name:
+            return fam
+    return "other"
+
+
+def source_sha(family: str) -> str:
+    import hashlib
+    for prefix, f in SOURCES.items():
+        if family.startswith(prefix):
+            path = os.path.join(ROOT, "tensor_transformer_layer_03_amd", "csrc", f)
+            return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    return ""
+
+
+def summarize_profiles(d: str, workload: str):
+    import csv
+    import collections
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    # kernel trace statistics
+    rows = list(csv.DictReader(open(os.path.join(d, "prof_c2", "c2_kernel_stats.csv"))))
+    fam = collections.defaultdict(lambda: [0, 0.0])
+    for r in rows:
+        f = kernel_family(r["Name"])
+        fam[f][0] += int(r["Calls"])
+        fam[f][1] += float(r["TotalDurationNs"])
+    total = sum(v[1] for v in fam.values())
+    lines = [f"# Kernel time, {workload} (rocprofv3 --kernel-trace --stats)", "",
+             "Command (repo root = <repo>, output dir = <out>):", "", "    " + PROFILE_CMDS["trace"], "",
+             "Every launch of the run (warm-up, timed and traced steps); all are whole passes, so the mix per",
+             "kernel family is the same as in one step.", "",
+             "| family | launches | total ms | avg us | share |", "|---|---|---|---|---|"]
+    for f, (c, t) in sorted(fam.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"| {f} | {c} | {t / 1e6:.3f} | {t / c / 1e3:.1f} | {100 * t / total:.1f}% |")
+    lines += ["", "Per instantiation (top 16):", "", "| kernel | calls | avg us | total ms |", "|---|---|---|---|"]
+    for r in rows[:16]:
+        lines.append(f"| {r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} |")
+    open(os.path.join(prof, f"kernel_stats_{workload}.md"), "w").write("\n".join(lines) + "\n")
+    # HBM bytes: FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a plain copy of known size
+    copy_bytes = 1024 * (1 << 20)
+    per = {}
+    scale = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cp = [float(r["Counter_Value"]) for r in csv.DictReader(open(os.path.join(d, f"pmc_{c}", "copy_counter_collection.csv")))
+              if "copyBuffer" in r["Kernel_Name"]]
+        scale[c] = copy_bytes / (sorted(cp)[len(cp) // 2] * 1024)
+        acc = collections.defaultdict(list)
+        for r in csv.DictReader(open(os.path.join(d, f"pmc_{c}", "bench_counter_collection.csv"))):
+            acc[kernel_family(r["Kernel_Name"])].append(float(r["Counter_Value"]) * 1024 * scale[c])
+        per[c] = {k: sum(v) / len(v) for k, v in acc.items()}
+    traffic = {f: {"fetch_bytes_per_launch": per["FETCH_SIZE"].get(f, 0.0),
+                   "write_bytes_per_launch": per["WRITE_SIZE"].get(f, 0.0),
+                   "bytes_per_launch": per["FETCH_SIZE"].get(f, 0.0) + per["WRITE_SIZE"].get(f, 0.0),
+                   "source_sha256": source_sha(f)} for f in per["FETCH_SIZE"]}
+    json.dump({"workload": workload, "scale": scale, "kernels": traffic},
+              open(os.path.join(prof, "hbm_traffic.json"), "w"), indent=1)
+    lines = [f"# HBM bytes per launch, {workload} (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+             "Commands:", "", "    " + PROFILE_CMDS["pmc"], "    " + PROFILE_CMDS["copy"], "",
+             f"Calibration: a {copy_bytes >> 20} MiB device copy reads and writes {copy_bytes >> 20} MiB; the counters "
+             f"read FETCH x{1 / scale['FETCH_SIZE']:.3f}, WRITE x{1 / scale['WRITE_SIZE']:.3f} of that, so bench "
+             f"bytes are scaled by {scale['FETCH_SIZE']:.3f} (fetch) and {scale['WRITE_SIZE']:.3f} (write).", "",
+             "| family | fetch MB/launch | write MB/launch | kernel source sha256 |", "|---|---|---|---|"]
+    for f, v in sorted(traffic.items(), key=lambda kv: -kv[1]["bytes_per_launch"]):
+        lines.append(f"| {f} | {v['fetch_bytes_per_launch'] / 1e6:.1f} | {v['write_bytes_per_launch'] / 1e6:.1f} | "
+                     f"{v['source_sha256']} |")
+    open(os.path.join(prof, f"hbm_traffic_{workload}.md"), "w").write("\n".join(lines) + "\n")
+    print(f"wrote profiles for {workload}")
+
+
+def measured_traffic(family: str):
+    """HBM bytes per launch from the committed counter summary, or None if the
+    kernel's source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(path))["kernels"][family]
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["bytes_per_launch"] if rec.get("source_sha256") == source_sha(family) else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,10 +267,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="gpt2_355m_t1")
     ap.add_argument("--trace-steps", type=int, default=3)
-    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the CPU-baseline sample (0 = skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=-1,
+                    help="sequences in the CPU-baseline sample (-1 = the whole micro-batch, 0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--layer-only", action="store_true", help="also time layer fwd+bwd without the loss")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 CSV output under DIR and exit")
     args = ap.parse_args()
 
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.config)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only: the TP group's ranks are computed on one device and the "
@@ -178,7 +302,8 @@ def main():
     for _ in range(args.warmup):
         st.step()
     ms = time_loop(st.step, args.steps, torch)
-    ms_layer = time_loop(lambda: (st.forward(), st.backward()), max(3, args.steps // 2), torch)
+    ms_layer = (time_loop(lambda: (st.forward(), st.backward()), max(3, args.steps // 2), torch)
+                if args.layer_only else None)
     agg = traced_kernels(st, args.trace_steps, B, cfg.dtype)
     loss = float(st.shared["loss"][0].item())
 
@@ -207,8 +332,9 @@ def main():
         },
         "pct_of_mfma_peak": round(100 * value / peak, 2),
         "flops_per_step": fl,
-        "layer_only": {"ms": round(ms_layer, 4), "tflops": round(fl["layer"] / (ms_layer / 1e3) / 1e12, 2),
-                       "note": "layer fwd+bwd with its 4 all-reduce stand-ins, loss excluded"},
+        "layer_only": None if ms_layer is None else {
+            "ms": round(ms_layer, 4), "tflops": round(fl["layer"] / (ms_layer / 1e3) / 1e12, 2),
+            "note": "layer fwd+bwd with its 4 all-reduce stand-ins, loss excluded"},
         "loss": round(loss, 6),
         "roofline": roofline(agg, cfg.dtype),
         "kernels_per_step": [{"kernel": k, "launches": c // args.trace_steps, "ms": round(t, 4),
@@ -216,8 +342,8 @@ def main():
                                   round(w / args.trace_steps / (t / 1e3) / (1e12 if k in MFMA_KERNELS else 1e9), 1)}
                              for k, c, t, w in kernels],
     }
-    if args.cpu_seqs > 0:
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seqs)
+    if args.cpu_seqs != 0:
+        out["cpu_baseline"] = cpu_baseline(cfg, cfg.micro_batch if args.cpu_seqs < 0 else args.cpu_seqs)
     print(json.dumps(out), flush=True)
 
 
