@@ -331,24 +331,68 @@ struct TileDma {
   }
 };
 
-// Loads of K-tile KT_ of both operands into stage S_; past the last tile the
-// buffers are zero-length (nothing is read, zeros are written).
-#define TPL_ISSUE_TILES(KT_, S_)                                                                                   \
-  do {                                                                                                             \
-    const int kt_ = (KT_);                                                                                         \
-    char* s_ = (S_);                                                                                               \
-    const bool live_ = kt_ * 64 < g.K;                                                                             \
-    if constexpr (A_K)                                                                                             \
-      dA.issue(g.A + (int64_t)m0 * g.lda * 2, live_ ? (int64_t)(g.M - m0) * g.lda * 2 : 0, kt_ * 128, s_, wave);  \
-    else                                                                                                           \
-      dA.issue(g.A + (int64_t)kt_ * 64 * g.lda * 2, live_ ? (int64_t)(g.K - kt_ * 64) * g.lda * 2 : 0, 0, s_,      \
-               wave);                                                                                              \
-    if constexpr (B_K)                                                                                             \
-      dB.issue(g.B + (int64_t)n0 * g.ldb * 2, live_ ? (int64_t)(g.N - n0) * g.ldb * 2 : 0, kt_ * 128,             \
-               s_ + BM * 128, wave);                                                                               \
-    else                                                                                                           \
-      dB.issue(g.B + (int64_t)kt_ * 64 * g.ldb * 2, live_ ? (int64_t)(g.K - kt_ * 64) * g.ldb * 2 : 0, 0,          \
-               s_ + BM * 128, wave);                                                                               \
+// Register-staged alternative for one operand tile: buffer_load_dwordx4 into
+// VGPRs (range-checked, zeros past the operand), then ds_write_b128 into the
+// same swizzled LDS layout as the direct-to-LDS path. Used where the compiler
+// cannot tell LDS-DMA writes of one stage from transpose reads of the other
+// and would otherwise wait for every load before each fragment read.
+template <int ROWS, bool KMAJ, int NT>
+struct TileReg {
+  static constexpr int kPer = ROWS * 8 / NT;   // 16-B chunks per thread
+  static_assert(kPer * NT == ROWS * 8, "tile does not split evenly over the threads");
+  u32x4 r[kPer];
+  int voff[kPer], loff[kPer];
+  __device__ __forceinline__ void init(int64_t ld, int row0, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = tid + i * NT;
+      if constexpr (KMAJ) {
+        const int row = p >> 3, c = p & 7;
+        voff[i] = (int)(((int64_t)row * ld + c * 8) * 2);
+        loff[i] = row * 128 + ((c ^ swz_k(row)) << 4);
+      } else {
+        constexpr int kC = ROWS / 8;
+        const int k = p / kC, c = p % kC;
+        voff[i] = (int)(((int64_t)k * ld + row0 + c * 8) * 2);
+        loff[i] = k * (ROWS * 2) + ((c ^ swz_t(k)) << 4);
+      }
+    }
+  }
+  __device__ __forceinline__ void load(const char* base, int64_t bytes, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the buffer-resource type exists only in the device pass
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], soff, 0);
+#endif
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) st16(lds + loff[i], r[i]);
+  }
+};
+
+// Loads of K-tile KT_ of both operands (into stage S_ for the direct-to-LDS
+// path, into registers otherwise); past the last tile the buffers are
+// zero-length (nothing is read, zeros are produced).
+#define TPL_TILE_ARGS_A(KT_)                                                                              \
+  (A_K ? g.A + (int64_t)m0 * g.lda * 2 : g.A + (int64_t)(KT_) * 64 * g.lda * 2),                         \
+      ((KT_) * 64 < g.K ? (A_K ? (int64_t)(g.M - m0) * g.lda * 2 : (int64_t)(g.K - (KT_) * 64) * g.lda * 2) \
+                        : 0),                                                                            \
+      (A_K ? (KT_) * 128 : 0)
+#define TPL_TILE_ARGS_B(KT_)                                                                              \
+  (B_K ? g.B + (int64_t)n0 * g.ldb * 2 : g.B + (int64_t)(KT_) * 64 * g.ldb * 2),                         \
+      ((KT_) * 64 < g.K ? (B_K ? (int64_t)(g.N - n0) * g.ldb * 2 : (int64_t)(g.K - (KT_) * 64) * g.ldb * 2) \
+                        : 0),                                                                            \
+      (B_K ? (KT_) * 128 : 0)
+#define TPL_ISSUE_TILES(KT_, S_)                                   \
+  do {                                                             \
+    if constexpr (DMA) {                                           \
+      tA.issue(TPL_TILE_ARGS_A(KT_), (S_), wave);                  \
+      tB.issue(TPL_TILE_ARGS_B(KT_), (S_) + BM * 128, wave);       \
+    } else {                                                       \
+      tA.load(TPL_TILE_ARGS_A(KT_));                               \
+      tB.load(TPL_TILE_ARGS_B(KT_));                               \
+    }                                                              \
   } while (0)
 
 // Fragment of tile row r0 + lane%32, k-slots 8*(lane/32)..+7 of step st.
@@ -404,9 +448,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
+constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
 
-template <int BM, int BN, int WGM, int WGN, bool A_K, bool B_K, int EPI, typename TC>
+template <int BM, int BN, int WGM, int WGN, bool A_K, bool B_K, bool DMA, int EPI, typename TC>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN, TM = WTM / 32, TN = WTN / 32;
@@ -428,10 +472,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
   const int m0 = (first_m + (logical % in_group) % gsize) * BM;
   const int n0 = ((logical % in_group) / gsize) * BN;
 
-  TileDma<BM, A_K, WGM * WGN> dA;
-  TileDma<BN, B_K, WGM * WGN> dB;
-  dA.init(g.lda, A_K ? 0 : m0, wave, lane);
-  dB.init(g.ldb, B_K ? 0 : n0, wave, lane);
+  using LA = typename std::conditional<DMA, TileDma<BM, A_K, WGM * WGN>, TileReg<BM, A_K, WGM * WGN * 64>>::type;
+  using LB = typename std::conditional<DMA, TileDma<BN, B_K, WGM * WGN>, TileReg<BN, B_K, WGM * WGN * 64>>::type;
+  LA tA;
+  LB tB;
+  if constexpr (DMA) {
+    tA.init(g.lda, A_K ? 0 : m0, wave, lane);
+    tB.init(g.ldb, B_K ? 0 : n0, wave, lane);
+  } else {
+    tA.init(g.lda, A_K ? 0 : m0, (int)threadIdx.x);
+    tB.init(g.ldb, B_K ? 0 : n0, (int)threadIdx.x);
+  }
 
 
   f32x16 acc[TM][TN];
@@ -445,13 +496,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
   Frag8<bf16> fa[2][TM], fb[2][TN];
   constexpr int kMf = TM * TN;                                // MFMAs per step
   constexpr int kRd = (TM + TN) * (A_K && B_K ? 1 : 2);        // LDS read instructions per step (upper bound)
-  constexpr int kDma = TileDma<BM, A_K, WGM * WGN>::kInst + TileDma<BN, B_K, WGM * WGN>::kInst;
+  constexpr int kVm = DMA ? TileDma<BM, A_K, WGM * WGN>::kInst + TileDma<BN, B_K, WGM * WGN>::kInst
+                          : TileReg<BM, A_K, WGM * WGN * 64>::kPer + TileReg<BN, B_K, WGM * WGN * 64>::kPer;
 
   const int KT = g.K / 64;                  // full K-tiles; a partial last tile is handled after the loop
   const int ktail = g.K & 63;
   const int kt_all = KT + (ktail ? 1 : 0);
 
   TPL_ISSUE_TILES(0, smem);
+  if constexpr (!DMA) {
+    tA.store(smem);
+    tB.store(smem + BM * 128);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   read_frags<BM, BN, A_K, B_K, TM, TN>(fa[0], fb[0], smem, 0, wm * WTM, wn * WTN, lane);
@@ -459,15 +515,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
   for (int kt = 0; kt < KT; ++kt) {
     const char* cur = smem + (kt & 1) * kStage;
     char* nxt = smem + ((kt + 1) & 1) * kStage;
-    // step 0: loads of the next tile + fragments of step 1, around 16 MFMAs
-    TPL_ISSUE_TILES(kt + 1, nxt);
+    // step 0: fragments of step 1 (first, so no LDS write is ordered before
+    // them), then the loads of the next tile, around this step's MFMAs
     read_frags<BM, BN, A_K, B_K, TM, TN>(fa[1], fb[1], cur, 1, wm * WTM, wn * WTN, lane);
+    TPL_ISSUE_TILES(kt + 1, nxt);
     mfma_tile<TM, TN>(acc, fa[0], fb[0]);
 #pragma unroll
     for (int x = 0; x < kMf; ++x) {
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      if (x < kDma) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
       if (x < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      if (x < kVm) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
     }
     // steps 1, 2
     read_frags<BM, BN, A_K, B_K, TM, TN>(fa[0], fb[0], cur, 2, wm * WTM, wn * WTN, lane);
@@ -478,11 +535,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
       if (x < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
     }
     read_frags<BM, BN, A_K, B_K, TM, TN>(fa[1], fb[1], cur, 3, wm * WTM, wn * WTN, lane);
+    if constexpr (!DMA) {   // stage `nxt` is free since the last barrier
+      tA.store(nxt);
+      tB.store(nxt + BM * 128);
+    }
     mfma_tile<TM, TN>(acc, fa[0], fb[0]);
 #pragma unroll
     for (int x = 0; x < kMf; ++x) {
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
       if (x < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      if (!DMA && x < kVm) __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
     }
     // step 3: a few MFMAs, then sync on the next tile, then its first fragments
     // are read while the remaining MFMAs of this step run
@@ -575,11 +637,10 @@ hipError_t run(const GemmDesc& d, hipStream_t s) {
 
 // Tile choice (measured on MI355X over the layer's shapes): the 256x256 tile
 // with 8 waves when it yields at least 384 workgroups (1.5 rounds over the
-// 256 CUs), otherwise 128x128 (two workgroups per CU); products with both
-// operands MN-major (weight gradients) use 128x128. TPL_GEMM_TILE=
+// 256 CUs), otherwise 128x128 (two workgroups per CU). TPL_GEMM_TILE=
 // 256x256[w8[t]] | 256x128[w8[t]] | 128x128 forces a shape (the tests use it
 // to cover every tile path).
-TileCfg choose_tile(int dtype, bool a_kmajor, bool b_kmajor, int64_t M, int64_t N) {
+TileCfg choose_tile(int dtype, int64_t M, int64_t N) {
   if (dtype == DT_F32) return {128, 128, 0};
   if (const char* f = getenv("TPL_GEMM_TILE")) {
     if (!strcmp(f, "256x256")) return {256, 256, 0};
@@ -590,7 +651,6 @@ TileCfg choose_tile(int dtype, bool a_kmajor, bool b_kmajor, int64_t M, int64_t 
     if (!strcmp(f, "256x128w8t")) return {256, 128, 4};
     if (!strcmp(f, "128x128")) return {128, 128, 0};
   }
-  if (!a_kmajor && !b_kmajor) return {128, 128, 0};
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
   if (big >= 384) return {256, 256, 1};
   return {128, 128, 0};
@@ -598,6 +658,7 @@ TileCfg choose_tile(int dtype, bool a_kmajor, bool b_kmajor, int64_t M, int64_t 
 
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BK_, int EPI, typename TC>
 hipError_t run_v2(const GemmDesc& d, hipStream_t s) {
+  constexpr bool kDma = AK && BK_;   // LDS-DMA for the forward products, register staging otherwise
   Args a;
   a.A = static_cast<const char*>(d.A); a.lda = d.lda;
   a.B = static_cast<const char*>(d.B); a.ldb = d.ldb;
@@ -609,7 +670,8 @@ hipError_t run_v2(const GemmDesc& d, hipStream_t s) {
   a.tiles_n = (a.N + BN - 1) / BN;
   const int nblk = a.tiles_m * a.tiles_n;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, AK, BK_, EPI, TC>), dim3(nblk), dim3(WGM * WGN * 64), 0, s, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, AK, BK_, kDma, EPI, TC>), dim3(nblk), dim3(WGM * WGN * 64), 0,
+                     s, a);
   return hipGetLastError();
 }
 
@@ -618,7 +680,7 @@ hipError_t run_tiles(const GemmDesc& d, hipStream_t s) {
   if constexpr (sizeof(T) == 4) {
     return run<T, 128, 128, 2, 2, AK, BK_, EPI, TC>(d, s);
   } else {
-    const TileCfg t = choose_tile(d.dtype, d.a_kmajor, d.b_kmajor, d.M, d.N);
+    const TileCfg t = choose_tile(d.dtype, d.M, d.N);
     switch (t.variant) {
       case 1: return run_v2<256, 256, 2, 4, AK, BK_, EPI, TC>(d, s);
       case 2: return run_v2<256, 256, 4, 2, AK, BK_, EPI, TC>(d, s);
