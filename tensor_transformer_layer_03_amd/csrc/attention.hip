@@ -535,6 +535,435 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(Args a) {
   }
 }
 
+// ------------------------------------------------------------------ bf16 kernels
+// bf16 version without register transposes. Every tile lives in LDS in its
+// natural [row][d] layout; transposed MFMA operands (V^T, K^T, Q^T, dO^T) are
+// read from it with ds_read_b64_tr_b16. To make the score accumulators come
+// out with keys (or queries) in natural order in each lane's k-slots, the
+// score MFMA's A operand takes tile row swap23(i) for accumulator row i (bits
+// 2 and 3 of the row offset swapped): accumulator element r of lane group g
+// then holds row 16*(r/8) + 8*g + r%8, which is exactly k-slot r%8 of the
+// next MFMA's step r/8 -- the layout a transpose read of the natural tile
+// delivers for the other operand.
+//
+// LDS rows are 8 (d=64) or 16 (d=96, 128; d=96 padded) 16-B chunks; chunk c
+// of row r sits at c ^ swz_a(r) within its aligned group of 8. swz_a maps the
+// rows read by any 8 consecutive lanes of a permuted row read
+// ({0..3, 8..11} + 16k or {4..7, 12..15} + 16k) and any 4 consecutive rows of
+// a transpose read to distinct 16-B bank groups.
+
+__device__ __forceinline__ int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+__device__ __forceinline__ int swz_a(int r) { return ((r & 3) << 1) | ((r >> 3) & 1); }
+
+typedef short s16x4 __attribute__((__vector_size__(8)));
+
+template <int D, int NT>
+struct NatTile {
+  static constexpr int kLC = D / 8;                  // 16-B chunks of data per row
+  static constexpr int kRC = D == 64 ? 8 : 16;       // chunks per LDS row
+  static constexpr int kRowBytes = kRC * 16;
+  static constexpr int kBytes = 64 * kRowBytes;
+  static constexpr int kTotal = 64 * kLC;
+  static constexpr int kPer = (kTotal + NT - 1) / NT;
+  u32x4 r[kPer];
+  __device__ __forceinline__ static int phys(int row, int c) { return (c & ~7) | ((c ^ swz_a(row)) & 7); }
+  // rows [row0, row0+64) of a head's [rows][d] block (row stride ld); rows >= nrows read as 0
+  __device__ __forceinline__ void load(const bf16* base, int64_t ld, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = tid + i * NT;
+      const int row = p / kLC, c = p % kLC;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (p < kTotal && row0 + row < nrows) v = ld16(base + (int64_t)(row0 + row) * ld + c * 8);
+      r[i] = v;
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = tid + i * NT;
+      if (p >= kTotal) break;
+      const int row = p / kLC, c = p % kLC;
+      st16(lds + row * kRowBytes + phys(row, c) * 16, r[i]);
+    }
+  }
+  // 8 consecutive d-values (chunk c) of one row
+  __device__ __forceinline__ static void row_frag(Frag8<bf16>& f, const char* lds, int row, int c) {
+    load_frag(f, reinterpret_cast<const bf16*>(lds + row * kRowBytes + phys(row, c) * 16));
+  }
+  // transposed fragment: lane (column mn0 + lane%32, group g) gets rows k0 + 8g .. k0 + 8g + 7
+  __device__ __forceinline__ static void tr_frag(Frag8<bf16>& f, const char* lds, int k0, int mn0, int lane) {
+    const int G = lane >> 4, s = lane & 15, e = s >> 2, q = s & 3;
+    const int mn = mn0 + 16 * (G & 1) + 4 * q;
+    const int k = k0 + 8 * (G >> 1) + e;                 // swz_a(k) == swz_a(k + 4)
+    const char* p0 = lds + k * kRowBytes + phys(k, mn >> 3) * 16 + (q & 1) * 8;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+    const s16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 4 * kRowBytes));
+    __builtin_memcpy(reinterpret_cast<char*>(&f.v), &lo, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&f.v) + 8, &hi, 8);
+  }
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(Args a) {
+  constexpr int NT = 256, BQ = 128, BKV = 64;
+  using Tile = NatTile<D, NT>;
+  __shared__ __attribute__((aligned(16))) char sK[2][Tile::kBytes];
+  __shared__ __attribute__((aligned(16))) char sV[2][Tile::kBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
+  const int qb = gridDim.x - 1 - blockIdx.x;   // heaviest causal blocks first
+  const int b = blockIdx.y / a.heads, hd = blockIdx.y % a.heads;
+  const int s = a.seq, hr = a.heads * D;
+  const bf16* Qg = reinterpret_cast<const bf16*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
+  const bf16* Kg = Qg + hr;
+  const bf16* Vg = Qg + 2 * hr;
+  const int q0 = qb * BQ, q0w = q0 + wave * 32, my_q = q0w + l32;
+  const float c = kLog2e * rsqrtf((float)D);
+  const int krow = swap23(l32);
+
+  Frag8<bf16> qf[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    if (my_q < s) load_frag(qf[st], Qg + (int64_t)my_q * a.ld_qkv + st * 16 + grp * 8);
+    else { float z[8] = {0, 0, 0, 0, 0, 0, 0, 0}; frag_from_f32(qf[st], z); }
+  }
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m = -INFINITY, l = 0.f;   // running max of raw scores, running sum
+
+  const int kv_end = CAUSAL ? min(s, q0 + BQ) : s;
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  Tile kl, vl;
+  kl.load(Kg, a.ld_qkv, 0, s, tid);
+  vl.load(Vg, a.ld_qkv, 0, s, tid);
+  kl.store(sK[0], tid);
+  vl.store(sV[0], tid);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1, kv0 = t * BKV;
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      kl.load(Kg, a.ld_qkv, kv0 + BKV, s, tid);
+      vl.load(Vg, a.ld_qkv, kv0 + BKV, s, tid);
+    }
+    if (!CAUSAL || kv0 <= q0w + 31) {
+      f32x16 sc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kt][r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+          Frag8<bf16> kf;
+          Tile::row_frag(kf, sK[cur], kt * 32 + krow, 2 * st + grp);
+          mfma_step(sc[kt], kf, qf[st]);
+        }
+      }
+      // key of accumulator element r of tile kt: kv0 + 32kt + 16(r/8) + 8grp + r%8
+      if ((CAUSAL && kv0 + BKV - 1 > q0w) || kv0 + BKV > s) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + 32 * kt + 16 * (r >> 3) + 8 * grp + (r & 7);
+            if (key >= s || (CAUSAL && key > my_q)) sc[kt][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kt][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m, mx);
+      const float mc = m_new == -INFINITY ? 0.f : m_new * c;
+      const float alpha = exp2f(m * c - mc);
+      float sum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2f(fmaf(sc[kt][r], c, -mc));
+          sc[kt][r] = p;
+          sum += p;
+        }
+      sum += __shfl_xor(sum, 32, kWave);
+      l = l * alpha + sum;
+      m = m_new;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        Frag8<bf16> pf;
+        acc_frag(pf, sc[ks >> 1], 8 * (ks & 1));
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          Frag8<bf16> vf;
+          Tile::tr_frag(vf, sV[cur], ks * 16, dt * 32, lane);
+          mfma_step(o[dt], vf, pf);
+        }
+      }
+    }
+    if (more) {
+      kl.store(sK[cur ^ 1], tid);
+      vl.store(sV[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  if (my_q < s) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16* Og = reinterpret_cast<bf16*>(a.ctx) + (int64_t)b * s * a.ld_ctx + hd * D;
+    store_rows<bf16, D>(Og, a.ld_ctx, my_q, o, inv, grp);
+    if (grp == 0) a.lse[((int64_t)b * a.heads + hd) * s + my_q] = (m * c) * kLn2 + logf(l);
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(Args a) {
+  constexpr int NT = 256, BQ = 128, BKV = 64;
+  using Tile = NatTile<D, NT>;
+  __shared__ __attribute__((aligned(16))) char sK[2][Tile::kBytes];
+  __shared__ __attribute__((aligned(16))) char sV[2][Tile::kBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
+  const int qb = gridDim.x - 1 - blockIdx.x;
+  const int b = blockIdx.y / a.heads, hd = blockIdx.y % a.heads;
+  const int s = a.seq, hr = a.heads * D;
+  const bf16* Qg = reinterpret_cast<const bf16*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
+  const bf16* Kg = Qg + hr;
+  const bf16* Vg = Qg + 2 * hr;
+  const bf16* dOg = reinterpret_cast<const bf16*>(a.dctx) + (int64_t)b * s * a.ld_ctx + hd * D;
+  const int q0 = qb * BQ, q0w = q0 + wave * 32, my_q = q0w + l32;
+  const float c = kLog2e * rsqrtf((float)D);
+  const int64_t stat = ((int64_t)b * a.heads + hd) * s;
+  const float lse_q = my_q < s ? a.lse[stat + my_q] * kLog2e : 0.f;
+  const float delta_q = my_q < s ? a.delta[stat + my_q] : 0.f;
+  const int krow = swap23(l32);
+
+  Frag8<bf16> qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    if (my_q < s) {
+      load_frag(qf[st], Qg + (int64_t)my_q * a.ld_qkv + st * 16 + grp * 8);
+      load_frag(df[st], dOg + (int64_t)my_q * a.ld_ctx + st * 16 + grp * 8);
+    } else {
+      float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      frag_from_f32(qf[st], z);
+      frag_from_f32(df[st], z);
+    }
+  }
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[dt][r] = 0.f;
+
+  const int kv_end = CAUSAL ? min(s, q0 + BQ) : s;
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  Tile kl, vl;
+  kl.load(Kg, a.ld_qkv, 0, s, tid);
+  vl.load(Vg, a.ld_qkv, 0, s, tid);
+  kl.store(sK[0], tid);
+  vl.store(sV[0], tid);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1, kv0 = t * BKV;
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      kl.load(Kg, a.ld_qkv, kv0 + BKV, s, tid);
+      vl.load(Vg, a.ld_qkv, kv0 + BKV, s, tid);
+    }
+    if (!CAUSAL || kv0 <= q0w + 31) {
+      f32x16 sc[2], dp[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { sc[kt][r] = 0.f; dp[kt][r] = 0.f; }
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+          Frag8<bf16> kf, vf;
+          Tile::row_frag(kf, sK[cur], kt * 32 + krow, 2 * st + grp);
+          Tile::row_frag(vf, sV[cur], kt * 32 + krow, 2 * st + grp);
+          mfma_step(sc[kt], kf, qf[st]);
+          mfma_step(dp[kt], vf, df[st]);
+        }
+      }
+      const bool mask = (CAUSAL && kv0 + BKV - 1 > q0w) || kv0 + BKV > s || my_q >= s;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = exp2f(fmaf(sc[kt][r], c, -lse_q));
+          if (mask) {
+            const int key = kv0 + 32 * kt + 16 * (r >> 3) + 8 * grp + (r & 7);
+            if (key >= s || (CAUSAL && key > my_q) || my_q >= s) p = 0.f;
+          }
+          sc[kt][r] = p * (dp[kt][r] - delta_q);   // dS^T
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        Frag8<bf16> sf;
+        acc_frag(sf, sc[ks >> 1], 8 * (ks & 1));
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          Frag8<bf16> kf;
+          Tile::tr_frag(kf, sK[cur], ks * 16, dt * 32, lane);
+          mfma_step(dq[dt], kf, sf);
+        }
+      }
+    }
+    if (more) {
+      kl.store(sK[cur ^ 1], tid);
+      vl.store(sV[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+  if (my_q < s) {
+    bf16* dQg = reinterpret_cast<bf16*>(a.dqkv) + (int64_t)b * s * a.ld_qkv + hd * D;
+    store_rows<bf16, D>(dQg, a.ld_qkv, my_q, dq, rsqrtf((float)D), grp);
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(Args a) {
+  constexpr int NT = 256, BKB = 128, BQ = 64;
+  using Tile = NatTile<D, NT>;
+  __shared__ __attribute__((aligned(16))) char sQ[2][Tile::kBytes];
+  __shared__ __attribute__((aligned(16))) char sdO[2][Tile::kBytes];
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sDl[2][BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
+  const int b = blockIdx.y / a.heads, hd = blockIdx.y % a.heads;
+  const int s = a.seq, hr = a.heads * D;
+  const bf16* Qg = reinterpret_cast<const bf16*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
+  const bf16* Kg = Qg + hr;
+  const bf16* Vg = Qg + 2 * hr;
+  const bf16* dOg = reinterpret_cast<const bf16*>(a.dctx) + (int64_t)b * s * a.ld_ctx + hd * D;
+  const int64_t stat = ((int64_t)b * a.heads + hd) * s;
+  const int k0 = blockIdx.x * BKB, k0w = k0 + wave * 32, my_k = k0w + l32;
+  const float c = kLog2e * rsqrtf((float)D);
+  const int qrow = swap23(l32);
+
+  Frag8<bf16> kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    if (my_k < s) {
+      load_frag(kf[st], Kg + (int64_t)my_k * a.ld_qkv + st * 16 + grp * 8);
+      load_frag(vf[st], Vg + (int64_t)my_k * a.ld_qkv + st * 16 + grp * 8);
+    } else {
+      float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      frag_from_f32(kf[st], z);
+      frag_from_f32(vf[st], z);
+    }
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dk[dt][r] = 0.f; dv[dt][r] = 0.f; }
+
+  const int qs = CAUSAL ? (k0 / BQ) * BQ : 0;
+  const int ntiles = s > qs ? (s - qs + BQ - 1) / BQ : 0;
+  Tile ql, dl;
+  auto stage_stats = [&](int buf, int q0) {
+    if (tid < BQ) {
+      const int q = q0 + tid;
+      sL[buf][tid] = q < s ? a.lse[stat + q] * kLog2e : 0.f;
+      sDl[buf][tid] = q < s ? a.delta[stat + q] : 0.f;
+    }
+  };
+  if (ntiles > 0) {
+    ql.load(Qg, a.ld_qkv, qs, s, tid);
+    dl.load(dOg, a.ld_ctx, qs, s, tid);
+    ql.store(sQ[0], tid);
+    dl.store(sdO[0], tid);
+    stage_stats(0, qs);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1, q0 = qs + t * BQ;
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      ql.load(Qg, a.ld_qkv, q0 + BQ, s, tid);
+      dl.load(dOg, a.ld_ctx, q0 + BQ, s, tid);
+    }
+    if (!CAUSAL || q0 + BQ - 1 >= k0w) {
+      f32x16 sc[2], dp[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { sc[qt][r] = 0.f; dp[qt][r] = 0.f; }
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+          Frag8<bf16> qf, df;
+          Tile::row_frag(qf, sQ[cur], qt * 32 + qrow, 2 * st + grp);
+          Tile::row_frag(df, sdO[cur], qt * 32 + qrow, 2 * st + grp);
+          mfma_step(sc[qt], qf, kf[st]);   // S[q][key], lane owns key
+          mfma_step(dp[qt], df, vf[st]);   // dP[q][key]
+        }
+      }
+      // query of accumulator element r of subtile qt: q0 + 32qt + 16(r/8) + 8grp + r%8
+      const bool mask = (CAUSAL && q0 < k0w + 31) || q0 + BQ > s || my_k >= s;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int qo = qt * 32 + 16 * (rq >> 1) + 8 * grp + 4 * (rq & 1);
+          const f32x4 lq = *reinterpret_cast<const f32x4*>(&sL[cur][qo]);
+          const f32x4 dq = *reinterpret_cast<const f32x4*>(&sDl[cur][qo]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rq + e;
+            float p = exp2f(fmaf(sc[qt][r], c, -lq[e]));
+            if (mask) {
+              const int q = q0 + qo + e;
+              if (q >= s || my_k >= s || (CAUSAL && my_k > q)) p = 0.f;
+            }
+            sc[qt][r] = p;                          // P
+            dp[qt][r] = p * (dp[qt][r] - dq[e]);    // dS
+          }
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        Frag8<bf16> pf, sf;
+        acc_frag(pf, sc[ks >> 1], 8 * (ks & 1));
+        acc_frag(sf, dp[ks >> 1], 8 * (ks & 1));
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          Frag8<bf16> of, qf;
+          Tile::tr_frag(of, sdO[cur], ks * 16, dt * 32, lane);
+          Tile::tr_frag(qf, sQ[cur], ks * 16, dt * 32, lane);
+          mfma_step(dv[dt], of, pf);
+          mfma_step(dk[dt], qf, sf);
+        }
+      }
+    }
+    if (more) {
+      ql.store(sQ[cur ^ 1], tid);
+      dl.store(sdO[cur ^ 1], tid);
+      stage_stats(cur ^ 1, q0 + BQ);
+    }
+    __syncthreads();
+  }
+  if (my_k < s) {
+    bf16* dKg = reinterpret_cast<bf16*>(a.dqkv) + (int64_t)b * s * a.ld_qkv + hr + hd * D;
+    store_rows<bf16, D>(dKg, a.ld_qkv, my_k, dk, rsqrtf((float)D), grp);
+    store_rows<bf16, D>(dKg + hr, a.ld_qkv, my_k, dv, 1.f, grp);
+  }
+}
+
 // Visible query-key pairs over all heads and sequences (causal: s(s+1)/2 each).
 double attn_pairs(const AttnDesc& d) {
   const double s = d.seq;
@@ -557,8 +986,13 @@ template <typename T, int D>
 hipError_t fwd_t(const AttnDesc& d, hipStream_t s) {
   Args a = make_args(d);
   dim3 grid((d.seq + 127) / 128, d.batch * d.heads);
-  if (d.causal) hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), grid, dim3(256), 0, s, a);
+  if constexpr (sizeof(T) == 2) {
+    if (d.causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (d.causal) hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -575,14 +1009,24 @@ hipError_t bwd_t(const AttnDesc& d, hipStream_t s) {
   dim3 grid((d.seq + 127) / 128, d.batch * d.heads);
   {
     TraceScope trace(K_ATTN_BWD_DKDV, s, 6.0 * attn_pairs(d) * d.head_dim);   // dV, dP, dK
-    if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false>), grid, dim3(256), 0, s, a);
+    if constexpr (sizeof(T) == 2) {
+      if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false>), grid, dim3(256), 0, s, a);
+    } else {
+      if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false>), grid, dim3(256), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   TraceScope trace(K_ATTN_BWD_DQ, s, 2.0 * attn_pairs(d) * d.head_dim);     // dQ
-  if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, false>), grid, dim3(256), 0, s, a);
+  if constexpr (sizeof(T) == 2) {
+    if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
