@@ -23,6 +23,7 @@
 //  * workgroups are renumbered so that consecutive tiles share an XCD (the
 //    dispatcher deals workgroups to the 8 XCDs round-robin, each with its own
 //    L2), then walked in groups of GROUP_M tile-rows for L2 reuse of B.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -288,7 +289,7 @@ typedef short s16x4 __attribute__((__vector_size__(8)));
 // Row swizzle of K-major tiles; depends on r mod 32 only, so the 32-row
 // fragments of a wave share one lane pattern.
 __device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 3); }
-__device__ __forceinline__ int swz_t(int k) { return 2 * (k & 3); }
+__device__ __forceinline__ int swz_t(int k) { return 4 * (k & 3); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
   const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
@@ -613,9 +614,205 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
   }
 }
 
+// ------------------------------------------- multi-stage K pipeline (K-major operands)
+// Forward (both operands K-major) products with a deeper prefetch: K-tiles of
+// 32 (64-B LDS rows), NS LDS stages, loads issued NS-1 tiles ahead straight
+// into LDS, and a partial wait (the NS-2 younger tiles stay in flight) before
+// the one barrier per K-tile. Four waves in a 2x2 grid. Row r of a 64-B-row
+// tile keeps chunk c at c ^ ((r >> 2) & 3): 16 consecutive rows, one chunk ->
+// 16 distinct 16-B bank groups.
+template <int ROWS, int NW>
+struct DmaK32 {   // ROWS x 64 B over NW waves: ROWS/(16 NW) instructions of 1 KB per wave
+  static constexpr int kInst = ROWS / (16 * NW);
+  int voff[kInst];
+  __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < kInst; ++j) {
+      const int r = 16 * (NW * j + wave) + (lane >> 2);
+      voff[j] = (int)(((int64_t)r * ld + (((lane & 3) ^ ((r >> 2) & 3)) << 3)) * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(const char* base, int64_t bytes, int soff, char* lds, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)   // the buffer-resource type exists only in the device pass
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+#pragma unroll
+    for (int j = 0; j < kInst; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (NW * j + wave) * 1024), 16, voff[j], soff, 0, 0);
+#endif
+  }
+};
+
+template <int TM, int TN>
+__device__ __forceinline__ void ms_read(Frag8<bf16> (&fa)[TM], Frag8<bf16> (&fb)[TN], const char* a, const char* b) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i) load_frag(fa[i], reinterpret_cast<const bf16*>(a + i * 2048));
+#pragma unroll
+  for (int j = 0; j < TN; ++j) load_frag(fb[j], reinterpret_cast<const bf16*>(b + j * 2048));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)" ::: "memory");
+  else if constexpr (N == 32) asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory");
+  else static_assert(N < 0, "unsupported wait count");
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, int OCC, int EPI, typename TC>
+__global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_ms_kernel(Args g) {
+  constexpr int NW = WGM * WGN;
+  constexpr int kStage = (BM + BN) * 64, kB = BM * 64;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;   // 32x32 fragments per wave
+  constexpr int kMf = TM * TN, kRd = TM + TN;
+  constexpr int kVm = DmaK32<BM, NW>::kInst + DmaK32<BN, NW>::kInst;   // loads per K-tile per wave
+  static_assert((NS & (NS - 1)) == 0 && NS >= 2, "stage count must be a power of two");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WGM, wn = wave / WGM;
+
+  const int nblk = g.tiles_m * g.tiles_n;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = nblk >> 3, rem = nblk & 7;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
+  const int in_group = kGroupM * g.tiles_n;
+  const int first_m = (logical / in_group) * kGroupM;
+  const int gsize = min(g.tiles_m - first_m, kGroupM);
+  const int m0 = (first_m + (logical % in_group) % gsize) * BM;
+  const int n0 = ((logical % in_group) / gsize) * BN;
+
+  DmaK32<BM, NW> tA;
+  DmaK32<BN, NW> tB;
+  tA.init(g.lda, wave, lane);
+  tB.init(g.ldb, wave, lane);
+  const char* baseA = g.A + (int64_t)m0 * g.lda * 2;
+  const char* baseB = g.B + (int64_t)n0 * g.ldb * 2;
+  const int64_t bytesA = (int64_t)(g.M - m0) * g.lda * 2, bytesB = (int64_t)(g.N - n0) * g.ldb * 2;
+#define TPL_MS_ISSUE(KT_)                                                                                \
+  do {                                                                                                   \
+    const bool live_ = (KT_) * 32 < g.K;                                                                 \
+    char* s_ = smem + ((KT_) & (NS - 1)) * kStage;                                                       \
+    tA.issue(baseA, live_ ? bytesA : 0, (KT_) * 64, s_, wave);                                           \
+    tB.issue(baseB, live_ ? bytesB : 0, (KT_) * 64, s_ + kB, wave);                                      \
+  } while (0)
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int rl = lane & 31;
+  const int aoff = (wm * WTM + rl) * 64, boff = kB + (wn * WTN + rl) * 64;
+  const int cx0 = ((lane >> 5) ^ ((rl >> 2) & 3)) << 4, cx1 = ((2 + (lane >> 5)) ^ ((rl >> 2) & 3)) << 4;
+  Frag8<bf16> fa[2][TM], fb[2][TN];
+
+  const int KT = g.K / 32;   // full K-tiles; a partial last tile is handled after the loop
+  const int ktail = g.K & 31;
+
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t) TPL_MS_ISSUE(t);
+  wait_vm_lgkm0<(NS - 2) * kVm>();   // tile 0 has landed (the younger ones may be in flight)
+  __builtin_amdgcn_s_barrier();
+  ms_read<TM, TN>(fa[0], fb[0], smem + aoff + cx0, smem + boff + cx0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const char* cur = smem + (kt & (NS - 1)) * kStage;
+    const char* nxt = smem + ((kt + 1) & (NS - 1)) * kStage;
+    // step 0: second k-step's fragments and the loads of tile kt+NS-1 around
+    // the first k-step's MFMAs (that stage was last read before the previous
+    // barrier)
+    ms_read<TM, TN>(fa[1], fb[1], cur + aoff + cx1, cur + boff + cx1);
+    TPL_MS_ISSUE(kt + NS - 1);
+    mfma_tile<TM, TN>(acc, fa[0], fb[0]);
+#pragma unroll
+    for (int x = 0; x < kMf; ++x) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (x < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      if (x < kVm) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1: a few MFMAs, then wait for tile kt+1 (the younger tiles stay in
+    // flight) and for this wave's reads of `cur`, barrier, then the next
+    // tile's first fragments under the remaining MFMAs
+    constexpr int kHead = kMf / 8 > 0 ? kMf / 8 : 1;
+#pragma unroll
+    for (int x = 0; x < kHead; ++x) mfma_step(acc[x / TN][x % TN], fb[1][x % TN], fa[1][x / TN]);
+    wait_vm_lgkm0<(NS - 2) * kVm>();
+    __builtin_amdgcn_s_barrier();
+    ms_read<TM, TN>(fa[0], fb[0], nxt + aoff + cx0, nxt + boff + cx0);
+#pragma unroll
+    for (int x = kHead; x < kMf; ++x) mfma_step(acc[x / TN][x % TN], fb[1][x % TN], fa[1][x / TN]);
+#pragma unroll
+    for (int x = kHead; x < kMf; ++x) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (x - kHead < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (ktail) {
+    // partial last tile (landed and barriered by the last iteration or the
+    // prologue): k-slots at or past K contribute zero
+    const char* cur = smem + (KT & (NS - 1)) * kStage;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ks > 0) ms_read<TM, TN>(fa[0], fb[0], cur + aoff + cx1, cur + boff + cx1);
+      if (KT * 32 + 16 * ks + 8 * (lane >> 5) >= g.K) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) zero_frag(fa[0][i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) zero_frag(fb[0][j]);
+      }
+      mfma_tile<TM, TN>(acc, fa[0], fb[0]);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
+#undef TPL_MS_ISSUE
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (n >= g.N) continue;
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
+          float b[4];
+          load4(reinterpret_cast<const bf16*>(g.bias) + n, b);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += b[e];
+        }
+        store4(reinterpret_cast<TC*>(g.C) + (int64_t)m * g.ldc + n, v[0], v[1], v[2], v[3]);
+        if constexpr (EPI == EPI_BIAS_GELU) {
+          bf16* ap = reinterpret_cast<bf16*>(g.C2) + (int64_t)m * g.ldc2 + n;
+          store4(ap, gelu_f(v[0]), gelu_f(v[1]), gelu_f(v[2]), gelu_f(v[3]));
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ dispatch
 
 struct TileCfg { int bm, bn, variant; };
+
+
 
 template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BK_, int EPI, typename TC>
 hipError_t run(const GemmDesc& d, hipStream_t s) {
@@ -635,12 +832,13 @@ hipError_t run(const GemmDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile choice (measured on MI355X over the layer's shapes): the 256x256 tile
-// with 8 waves when it yields at least 384 workgroups (1.5 rounds over the
-// 256 CUs), otherwise 128x128 (two workgroups per CU). TPL_GEMM_TILE=
-// 256x256[w8[t]] | 256x128[w8[t]] | 128x128 forces a shape (the tests use it
-// to cover every tile path).
-TileCfg choose_tile(int dtype, int64_t M, int64_t N) {
+// Tile choice (measured on MI355X over the layer's shapes): forward products
+// with at least 1024 tiles of 256x256 (the logits) take the four-stage 32-deep
+// K pipeline; otherwise the 256x256 tile with 8 waves when it yields at least
+// 384 workgroups (1.5 rounds over the 256 CUs), else 128x128 (two workgroups
+// per CU). TPL_GEMM_TILE=256x256[w8[t]] | 256x128[w8[t]] | 128x128 |
+// 256x256w8s4 forces a shape (the tests use it to cover every tile path).
+TileCfg choose_tile(int dtype, bool nt, int64_t M, int64_t N) {
   if (dtype == DT_F32) return {128, 128, 0};
   if (const char* f = getenv("TPL_GEMM_TILE")) {
     if (!strcmp(f, "256x256")) return {256, 256, 0};
@@ -650,8 +848,10 @@ TileCfg choose_tile(int dtype, int64_t M, int64_t N) {
     if (!strcmp(f, "256x128w8")) return {256, 128, 3};
     if (!strcmp(f, "256x128w8t")) return {256, 128, 4};
     if (!strcmp(f, "128x128")) return {128, 128, 0};
+    if (!strcmp(f, "256x256w8s4")) return {256, 256, nt ? 5 : 1};
   }
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  if (nt && big >= 1024) return {256, 256, 5};
   if (big >= 384) return {256, 256, 1};
   return {128, 128, 0};
 }
@@ -675,17 +875,37 @@ hipError_t run_v2(const GemmDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WGM, int WGN, int NS, int OCC, int EPI, typename TC>
+hipError_t run_ms(const GemmDesc& d, hipStream_t s) {
+  Args a;
+  a.A = static_cast<const char*>(d.A); a.lda = d.lda;
+  a.B = static_cast<const char*>(d.B); a.ldb = d.ldb;
+  a.C = static_cast<char*>(d.C); a.ldc = d.ldc;
+  a.C2 = static_cast<char*>(d.C2); a.ldc2 = d.ldc2;
+  a.bias = static_cast<const char*>(d.bias);
+  a.M = (int)d.M; a.N = (int)d.N; a.K = (int)d.K;
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.tiles_n = (a.N + BN - 1) / BN;
+  const int nblk = a.tiles_m * a.tiles_n;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_ms_kernel<BM, BN, WGM, WGN, NS, OCC, EPI, TC>), dim3(nblk), dim3(WGM * WGN * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, bool AK, bool BK_, int EPI, typename TC>
 hipError_t run_tiles(const GemmDesc& d, hipStream_t s) {
   if constexpr (sizeof(T) == 4) {
     return run<T, 128, 128, 2, 2, AK, BK_, EPI, TC>(d, s);
   } else {
-    const TileCfg t = choose_tile(d.dtype, d.M, d.N);
+    const TileCfg t = choose_tile(d.dtype, AK && BK_, d.M, d.N);
     switch (t.variant) {
       case 1: return run_v2<256, 256, 2, 4, AK, BK_, EPI, TC>(d, s);
       case 2: return run_v2<256, 256, 4, 2, AK, BK_, EPI, TC>(d, s);
       case 3: return run_v2<256, 128, 2, 4, AK, BK_, EPI, TC>(d, s);
       case 4: return run_v2<256, 128, 4, 2, AK, BK_, EPI, TC>(d, s);
+      case 5:
+        if constexpr (AK && BK_) return run_ms<256, 256, 2, 4, 4, 2, EPI, TC>(d, s);
+        break;
       default: break;
     }
     if (t.bm == 256 && t.bn == 256) return run_v2<256, 256, 2, 2, AK, BK_, EPI, TC>(d, s);

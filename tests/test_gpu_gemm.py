@@ -50,7 +50,7 @@ def test_gemm(case):
 
 
 TILE_CASES = [(lay, tile) for lay in ((1, 1), (1, 0), (0, 0))
-              for tile in ("256x256", "256x256w8", "256x256w8t", "256x128", "256x128w8", "256x128w8t", "128x128")]
+              for tile in ("256x256", "256x256w8", "256x256w8t", "256x128", "256x128w8", "256x128w8t", "128x128", "256x256w8s4")]
 
 
 @pytest.mark.parametrize("lay,tile", TILE_CASES, ids=lambda c: str(c))
@@ -59,3 +59,12 @@ def test_gemm_every_tile_shape(lay, tile, monkeypatch):
     monkeypatch.setenv("TPL_GEMM_TILE", tile)
     ak, bk = lay
     test_gemm(("bf16", ak, bk, 520, 776, 328, ak and bk))
+
+
+@pytest.mark.parametrize("shape", [(4200, 4200, 96), (4104, 4296, 32), (2056, 8200, 1064)], ids=lambda c: str(c))
+def test_gemm_multistage(shape, monkeypatch):
+    """The four-stage forward kernel on more tiles than workgroups, with fewer
+    K-tiles than pipeline stages, a ragged K tail and ragged M and N."""
+    monkeypatch.setenv("TPL_GEMM_TILE", "256x256w8s4")
+    M, N, K = shape
+    test_gemm(("bf16", 1, 1, M, N, K, True))
