@@ -8,14 +8,14 @@
 // All of these are HBM-bound: they stream each operand once with 16-byte
 // vector accesses. LayerNorm uses one wave per row with the row cached in
 // registers (two-pass mean / variance, no LDS); column sums run in two
-// deterministic stages (per row-chunk partials, then a fixed-order sum).
+// deterministic stages (per 32-row-chunk partials, then a fixed-order sum).
 #include "common.h"
 #include "kernels.h"
 
 namespace tpl {
 namespace {
 
-constexpr int kRowsPerChunk = 64;
+constexpr int kRowsPerChunk = 32;
 
 template <typename T>
 __device__ __forceinline__ void unpack(const u32x4& raw, float* v) {
@@ -144,88 +144,96 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const T* __restrict__ dy, c
   }
 }
 
-// Column partials for LN backward: ws[chunk][0][c] = sum dsum*xhat,
-// ws[chunk][1][c] = sum dsum, ws[chunk][2][c] = sum dy over the chunk's rows.
-template <typename T>
-__global__ __launch_bounds__(64) void ln_bwd_cols_kernel(const T* __restrict__ dy, const T* __restrict__ dsum,
-                                                         const T* __restrict__ x, const float* __restrict__ mu,
-                                                         const float* __restrict__ rstd, float* __restrict__ ws,
-                                                         int64_t rows, int cols) {
+// Column partials. A workgroup covers 64 column chunks of 16 B and the
+// kRowsPerChunk rows of one row chunk; wave w takes rows w, w+4, ... and the
+// four wave sums are added in wave order through LDS, so every partial has a
+// fixed summation order.
+//   NOUT == 1: ws[chunk][0][c] = sum X[r][c]                       (bias gradients)
+//   NOUT == 3: ws[chunk][0][c] = sum dsum*xhat, [1] = sum dsum, [2] = sum dy
+//              (LN gamma / beta gradients and the next bias gradient)
+template <typename T, int NOUT>
+__global__ __launch_bounds__(256) void colpart_kernel(const T* __restrict__ X, int64_t ld,
+                                                      const T* __restrict__ dy, const T* __restrict__ x,
+                                                      const float* __restrict__ mu, const float* __restrict__ rstd,
+                                                      float* __restrict__ ws, int64_t rows, int cols) {
   constexpr int V = Vec16<T>::N;
-  const int ch = blockIdx.x * 64 + threadIdx.x;
-  if (ch * V >= cols) return;
+  __shared__ float part[4][NOUT][64 * V];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ch = blockIdx.x * 64 + lane;
+  const bool live = ch * V < cols;
   const int64_t r0 = (int64_t)blockIdx.y * kRowsPerChunk;
   const int64_t r1 = min<int64_t>(rows, r0 + kRowsPerChunk);
-  float a[V], b[V], c[V];
+  float a[NOUT][V];
 #pragma unroll
-  for (int e = 0; e < V; ++e) { a[e] = 0.f; b[e] = 0.f; c[e] = 0.f; }
-  for (int64_t r = r0; r < r1; ++r) {
-    float dv[V], xv[V], yv[V];
-    unpack<T>(ld16(dsum + r * cols + ch * V), dv);
-    unpack<T>(ld16(x + r * cols + ch * V), xv);
-    unpack<T>(ld16(dy + r * cols + ch * V), yv);
-    const float m = mu[r], rs = rstd[r];
+  for (int k = 0; k < NOUT; ++k)
 #pragma unroll
-    for (int e = 0; e < V; ++e) {
-      a[e] += dv[e] * (xv[e] - m) * rs;
-      b[e] += dv[e];
-      c[e] += yv[e];
+    for (int e = 0; e < V; ++e) a[k][e] = 0.f;
+  if (live) {
+#pragma unroll 4
+    for (int64_t r = r0 + wave; r < r1; r += 4) {
+      float v[V];
+      unpack<T>(ld16(X + r * ld + ch * V), v);   // NOUT == 3: X = dsum
+      if constexpr (NOUT == 1) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) a[0][e] += v[e];
+      } else {
+        float xv[V], yv[V];
+        unpack<T>(ld16(x + r * ld + ch * V), xv);
+        unpack<T>(ld16(dy + r * ld + ch * V), yv);
+        const float m = mu[r], rs = rstd[r];
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          a[0][e] += v[e] * (xv[e] - m) * rs;
+          a[1][e] += v[e];
+          a[2][e] += yv[e];
+        }
+      }
     }
   }
-  float* w = ws + (int64_t)blockIdx.y * 3 * cols + ch * V;
 #pragma unroll
-  for (int e = 0; e < V; ++e) { w[e] = a[e]; w[cols + e] = b[e]; w[2 * cols + e] = c[e]; }
-}
-
-// Column partials of one matrix: ws[chunk][c] = sum over the chunk's rows of X[r][c].
-template <typename T>
-__global__ __launch_bounds__(64) void colsum_kernel(const T* __restrict__ X, int64_t ld, int64_t rows,
-                                                    int cols, float* __restrict__ ws) {
-  constexpr int V = Vec16<T>::N;
-  const int ch = blockIdx.x * 64 + threadIdx.x;
-  if (ch * V >= cols) return;
-  const int64_t r0 = (int64_t)blockIdx.y * kRowsPerChunk;
-  const int64_t r1 = min<int64_t>(rows, r0 + kRowsPerChunk);
-  float a[V];
+  for (int k = 0; k < NOUT; ++k)
 #pragma unroll
-  for (int e = 0; e < V; ++e) a[e] = 0.f;
-  for (int64_t r = r0; r < r1; ++r) {
-    float v[V];
-    unpack<T>(ld16(X + r * ld + ch * V), v);
-#pragma unroll
-    for (int e = 0; e < V; ++e) a[e] += v[e];
+    for (int e = 0; e < V; ++e) part[wave][k][e * 64 + lane] = a[k][e];
+  __syncthreads();
+  // 64*V columns x NOUT outputs, 256 threads: thread t finishes column slots t, t+256, ...
+  const int64_t chunk = blockIdx.y;
+  for (int idx = threadIdx.x; idx < NOUT * 64 * V; idx += 256) {
+    const int k = idx / (64 * V), q = idx % (64 * V);
+    const int e = q / 64, l = q % 64;
+    const int c = (blockIdx.x * 64 + l) * V + e;
+    if (c < cols)
+      ws[(chunk * NOUT + k) * cols + c] = (part[0][k][q] + part[1][k][q]) + (part[2][k][q] + part[3][k][q]);
   }
-  float* w = ws + (int64_t)blockIdx.y * cols + ch * V;
-#pragma unroll
-  for (int e = 0; e < V; ++e) w[e] = a[e];
 }
 
-// out_k[c] = sum over chunks of ws[chunk][k][c], for k < nout. One block of
-// 4 waves per 64 columns: wave w sums chunks w, w+4, ... (lane = column), the
-// four wave sums are then added in wave order -- a fixed order, so the result
-// is deterministic.
-__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ ws, int nchunks, int cols,
-                                                           int nout, float* o0, float* o1, float* o2) {
-  __shared__ float part[3][4][64];
+// out_k[c] = sum over chunks of ws[chunk][k][c], for k < nout. One workgroup
+// of 16 waves per 64 columns and output: wave w sums chunks w, w+16, ... with
+// four accumulators (lane = column), then the sixteen wave sums are added in
+// a fixed tree order, so the result is deterministic.
+__global__ __launch_bounds__(1024) void colsum_final_kernel(const float* __restrict__ ws, int nchunks, int cols,
+                                                            int nout, float* o0, float* o1, float* o2) {
+  __shared__ float part[16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lane;
-  for (int k = 0; k < nout; ++k) {
-    float s0 = 0.f, s1 = 0.f;
-    if (c < cols) {
-      int i = wave;
-      for (; i + 4 < nchunks; i += 8) {
-        s0 += ws[((int64_t)i * nout + k) * cols + c];
-        s1 += ws[((int64_t)(i + 4) * nout + k) * cols + c];
-      }
-      if (i < nchunks) s0 += ws[((int64_t)i * nout + k) * cols + c];
+  const int k = blockIdx.y;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  if (c < cols) {
+    int i = wave;
+    for (; i + 48 < nchunks; i += 64) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s[u] += ws[((int64_t)(i + 16 * u) * nout + k) * cols + c];
     }
-    part[k][wave][lane] = s0 + s1;
+    for (; i < nchunks; i += 16) s[0] += ws[((int64_t)i * nout + k) * cols + c];
   }
+  part[wave][lane] = (s[0] + s[1]) + (s[2] + s[3]);
   __syncthreads();
   if (wave == 0 && c < cols) {
-    float* outs[3] = {o0, o1, o2};
-    for (int k = 0; k < nout; ++k)
-      outs[k][c] = (part[k][0][lane] + part[k][1][lane]) + (part[k][2][lane] + part[k][3][lane]);
+    float q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      q[u] = (part[4 * u][lane] + part[4 * u + 1][lane]) + (part[4 * u + 2][lane] + part[4 * u + 3][lane]);
+    float* out = k == 0 ? o0 : (k == 1 ? o1 : o2);
+    out[c] = (q[0] + q[1]) + (q[2] + q[3]);
   }
 }
 
@@ -335,16 +343,17 @@ hipError_t launch_layernorm_bwd(int dtype, const void* dy, const void* dsum, con
     const int v = dtype == DT_BF16 ? 8 : 4;
     dim3 grid((cols / v + 63) / 64, (unsigned)n_chunks(rows));
     if (dtype == DT_BF16)
-      hipLaunchKernelGGL(ln_bwd_cols_kernel<bf16>, grid, dim3(64), 0, s, static_cast<const bf16*>(dy),
-                         static_cast<const bf16*>(dsum), static_cast<const bf16*>(x), mu, rstd, ws, rows, cols);
+      hipLaunchKernelGGL((colpart_kernel<bf16, 3>), grid, dim3(256), 0, s, static_cast<const bf16*>(dsum), (int64_t)cols,
+                         static_cast<const bf16*>(dy), static_cast<const bf16*>(x), mu, rstd, ws, rows, cols);
     else
-      hipLaunchKernelGGL(ln_bwd_cols_kernel<float>, grid, dim3(64), 0, s, static_cast<const float*>(dy),
-                         static_cast<const float*>(dsum), static_cast<const float*>(x), mu, rstd, ws, rows, cols);
+      hipLaunchKernelGGL((colpart_kernel<float, 3>), grid, dim3(256), 0, s, static_cast<const float*>(dsum),
+                         (int64_t)cols, static_cast<const float*>(dy), static_cast<const float*>(x), mu, rstd, ws,
+                         rows, cols);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {
     TraceScope trace(K_COLSUM_FINAL, s);
-    hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64), dim3(256), 0, s, ws, (int)n_chunks(rows), cols,
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64, 3), dim3(1024), 0, s, ws, (int)n_chunks(rows), cols,
                        3, d_g, d_b, d_bout);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -360,13 +369,15 @@ hipError_t launch_colsum(int dtype, const void* X, int64_t ld, int64_t rows, int
     const int v = dtype == DT_BF16 ? 8 : 4;
     dim3 grid((cols / v + 63) / 64, (unsigned)n_chunks(rows));
     if (dtype == DT_BF16)
-      hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(64), 0, s, static_cast<const bf16*>(X), ld, rows, cols, ws);
+      hipLaunchKernelGGL((colpart_kernel<bf16, 1>), grid, dim3(256), 0, s, static_cast<const bf16*>(X), ld, nullptr,
+                         nullptr, nullptr, nullptr, ws, rows, cols);
     else
-      hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(64), 0, s, static_cast<const float*>(X), ld, rows, cols, ws);
+      hipLaunchKernelGGL((colpart_kernel<float, 1>), grid, dim3(256), 0, s, static_cast<const float*>(X), ld, nullptr,
+                         nullptr, nullptr, nullptr, ws, rows, cols);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   TraceScope trace(K_COLSUM_FINAL, s);
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64), dim3(256), 0, s, ws, (int)n_chunks(rows), cols, 1,
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64, 1), dim3(1024), 0, s, ws, (int)n_chunks(rows), cols, 1,
                      out, nullptr, nullptr);
   return hipGetLastError();
 }

@@ -19,24 +19,38 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 }
 
 // One workgroup per row: stats[row] = (max, sum exp(l - max), target logit or 0).
+// Each thread takes chunks of 16 B in groups of kU (loads of a group issued
+// together, then merged into the running (max, sum)), so enough bytes are in
+// flight to stream the logits at HBM rate.
 template <typename T>
 __global__ __launch_bounds__(256) void xent_stats_kernel(const T* __restrict__ logits, int vr,
                                                          const int32_t* __restrict__ targets, int64_t v0,
                                                          float* __restrict__ stats) {
-  constexpr int V = Vec16<T>::N;
+  constexpr int V = Vec16<T>::N, kU = 4;
   const int64_t row = blockIdx.x;
   const T* lr = logits + row * vr;
+  const int nch = vr / V;
   float m = -INFINITY, s = 0.f;
-  for (int ch = threadIdx.x; ch < vr / V; ch += 256) {
-    Vec16<T> x;
-    x.raw = ld16(lr + ch * V);
-    float v[V], mx = -INFINITY;
+  for (int base = threadIdx.x; base < nch; base += 256 * kU) {
+    Vec16<T> x[kU];
 #pragma unroll
-    for (int e = 0; e < V; ++e) { v[e] = to_f32(x.get(e)); mx = fmaxf(mx, v[e]); }
+    for (int u = 0; u < kU; ++u) {
+      const int ch = base + 256 * u;
+      if (ch < nch) x[u].raw = ld16(lr + ch * V);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (base + 256 * u < nch)
+#pragma unroll
+        for (int e = 0; e < V; ++e) mx = fmaxf(mx, to_f32(x[u].get(e)));
     const float mn = fmaxf(m, mx);
     float acc = s * __expf(m - mn);
 #pragma unroll
-    for (int e = 0; e < V; ++e) acc += __expf(v[e] - mn);
+    for (int u = 0; u < kU; ++u)
+      if (base + 256 * u < nch)
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc += __expf(to_f32(x[u].get(e)) - mn);
     m = mn;
     s = acc;
   }
@@ -100,29 +114,41 @@ __global__ __launch_bounds__(1024) void xent_finish_kernel(StatPtrs st, int t, i
 }
 
 // In place: l <- g (exp(l - lse) - [j == target - v0]), g = dloss * mask / count.
+// Chunks are processed kU at a time (loads issued together) for bytes in flight.
 template <typename T>
 __global__ __launch_bounds__(256) void xent_dlogits_kernel(T* logits, int vr, const int32_t* __restrict__ targets,
                                                            int64_t v0, const uint8_t* __restrict__ mask,
                                                            const float* __restrict__ lse,
                                                            const float* __restrict__ loss, float dloss) {
-  constexpr int V = Vec16<T>::N;
+  constexpr int V = Vec16<T>::N, kU = 4;
   const int64_t row = blockIdx.x;
   T* lr = logits + row * vr;
+  const int nch = vr / V;
   const float cnt = loss[1];
   const float g = (mask ? (float)mask[row] : 1.f) * (cnt > 0.f ? dloss / cnt : 0.f);
   const float L = lse[row];
   const int64_t t = (int64_t)targets[row] - v0;
-  for (int ch = threadIdx.x; ch < vr / V; ch += 256) {
-    Vec16<T> x;
-    x.raw = ld16(lr + ch * V);
+  for (int base = threadIdx.x; base < nch; base += 256 * kU) {
+    Vec16<T> x[kU];
 #pragma unroll
-    for (int e = 0; e < V; ++e) {
-      const int j = ch * V + e;
-      float p = __expf(to_f32(x.get(e)) - L);
-      if (j == t) p -= 1.f;
-      x.set(e, from_f32<T>(g * p));
+    for (int u = 0; u < kU; ++u) {
+      const int ch = base + 256 * u;
+      if (ch < nch) x[u].raw = ld16(lr + ch * V);
     }
-    st16(lr + ch * V, x.raw);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int ch = base + 256 * u;
+      if (ch < nch) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const int j = ch * V + e;
+          float p = __expf(to_f32(x[u].get(e)) - L);
+          if (j == t) p -= 1.f;
+          x[u].set(e, from_f32<T>(g * p));
+        }
+        st16(lr + ch * V, x[u].raw);
+      }
+    }
   }
 }
 
