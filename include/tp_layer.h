@@ -159,15 +159,25 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
                               const tpl_block_params* params, void* saved, void* d_ln_partial,
                               void* dx, const tpl_block_grads* grads, void* stream);
 
+/* Size in bytes of the `stats` buffer of vocab_parallel_xent_fwd for this
+ * descriptor (0 if the descriptor is invalid). Its first N*3 floats are the
+ * row statistics exchanged between ranks; the rest is scratch for the
+ * per-tile statistics of the logits product (bf16). */
+size_t vocab_parallel_xent_stats_bytes(const tpl_desc* desc);
+
 /* Vocabulary-parallel cross-entropy forward (guide page 3.3; podcast page
  * Outline: output embedding split along the vocabulary, loss fused).
  *   TPL_XENT_LOCAL: logits = hidden E_r^T ([N][V_r], storage dtype, kept for
  *     the backward) and per-row statistics stats[n] = (m, se, tl):
  *     m = max_j logits[n][j], se = sum_j exp(logits[n][j] - m),
  *     tl = logits[n][targets[n] - rank*V_r] if the target is in this rank's
- *     range, else 0. The shard's softmax is never materialised.
+ *     range, else 0, over the stored (rounded) logits. The shard's softmax is
+ *     never materialised: in bf16 the statistics are taken in the product's
+ *     epilogue per 256- or 128-column tile and merged per row in a fixed
+ *     order. `stats` must hold vocab_parallel_xent_stats_bytes(desc) bytes.
  *   TPL_XENT_FINISH: from the t ranks' stats (all_stats: HOST array of t device
- *     pointers, in rank order): M = max_r m_r, S = sum_r se_r exp(m_r - M),
+ *     pointers, in rank order; only the first N*3 floats of each are read):
+ *     M = max_r m_r, S = sum_r se_r exp(m_r - M),
  *     lse[n] = M + ln S, loss_rows[n] = mask[n] * (lse[n] - sum_r tl_r),
  *     loss[0] = sum_n loss_rows[n] / sum_n mask[n], loss[1] = sum_n mask[n].
  * hidden: [N][h]; emb: E_r [V_r][h]; targets: [N] int32 global ids in [0, V)

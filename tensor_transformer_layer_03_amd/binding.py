@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         P = ctypes.POINTER
         L.tp_layer_saved_bytes.restype = ctypes.c_size_t
         L.tp_layer_saved_bytes.argtypes = [P(TplDesc), ctypes.c_int]
+        L.vocab_parallel_xent_stats_bytes.restype = ctypes.c_size_t
+        L.vocab_parallel_xent_stats_bytes.argtypes = [P(TplDesc)]
         L.tp_layer_shard_fwd.argtypes = [P(TplDesc), ctypes.c_int, _VP, P(TplBlockParams), _VP, _VP, _VP]
         L.shard_partial_sum.argtypes = [P(TplDesc), P(ctypes.c_void_p), _I32, _VP, _VP, _VP, _I64, _I32, _VP]
         L.tp_layer_shard_bwd.argtypes = [P(TplDesc), ctypes.c_int, ctypes.c_int, _VP, _VP, _VP,
@@ -88,7 +90,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("tp_layer_saved_bytes", "tp_layer_shard_fwd", "shard_partial_sum", "tp_layer_shard_bwd",
-            "vocab_parallel_xent_fwd", "vocab_parallel_xent_bwd", "tpl_gemm", "tpl_trace_enable",
+            "vocab_parallel_xent_stats_bytes", "vocab_parallel_xent_fwd", "vocab_parallel_xent_bwd", "tpl_gemm", "tpl_trace_enable",
             "tpl_trace_read", "tpl_trace_kernel_name", "tpl_status_string")
 
 
@@ -135,6 +137,10 @@ def block_grads(d_w_in=None, d_b_in=None, d_w_out=None, d_ln_g=None, d_ln_b=None
 
 def tp_layer_saved_bytes(desc: TplDesc, block: int) -> int:
     return int(lib().tp_layer_saved_bytes(ctypes.byref(desc), block))
+
+
+def vocab_parallel_xent_stats_bytes(desc: TplDesc) -> int:
+    return int(lib().vocab_parallel_xent_stats_bytes(ctypes.byref(desc)))
 
 
 def tp_layer_shard_fwd(desc, block, x, params: TplBlockParams, partial, saved, stream=None):

@@ -119,6 +119,9 @@ P* slot(void* base, const Saved& s, int i) {
   return reinterpret_cast<P*>(static_cast<char*>(base) + s.off[i]);
 }
 
+// Row statistics [N][3] at the head of the xent statistics buffer, padded to 256 B.
+size_t xent_head_floats(int64_t rows) { return (size_t)((rows * 3 + 63) / 64) * 64; }
+
 GemmDesc gemm(const Dims& m, bool ak, bool bk, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
               const void* B, int64_t ldb, void* C, int64_t ldc) {
   GemmDesc g{};
@@ -146,7 +149,7 @@ int g_trace_cap = 0, g_trace_used = 0;
 const char* const kKernelNames[K_COUNT] = {
     "gemm_nt", "gemm_nn", "gemm_tn", "attn_fwd", "attn_bwd_pre", "attn_bwd_dq", "attn_bwd_dkdv",
     "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_cols", "colsum", "colsum_final", "partial_sum",
-    "xent_stats", "xent_finish", "xent_dlogits"};
+    "xent_stats", "xent_finish", "xent_dlogits", "xent_merge"};
 
 }  // namespace
 
@@ -347,6 +350,14 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
   return TPL_OK;
 }
 
+size_t vocab_parallel_xent_stats_bytes(const tpl_desc* desc) {
+  Dims m;
+  if (check_desc(desc, &m) != TPL_OK) return 0;
+  size_t floats = xent_head_floats(m.N);
+  if (xent_gemm_tile_cols(m.dt, m.N, m.vr) > 0) floats += xent_part_floats(m.N, m.vr);
+  return floats * sizeof(float);
+}
+
 tpl_status vocab_parallel_xent_fwd(const tpl_desc* desc, tpl_xent_phase phase, const void* hidden, const void* emb,
                                    const int32_t* targets, const uint8_t* loss_mask, void* logits, float* stats,
                                    const float* const* all_stats, float* lse, float* loss_rows, float* loss,
@@ -358,7 +369,19 @@ tpl_status vocab_parallel_xent_fwd(const tpl_desc* desc, tpl_xent_phase phase, c
   if (phase == TPL_XENT_LOCAL) {
     if (!ok_ptr(hidden) || !ok_ptr(emb) || !ok_ptr(targets) || !ok_ptr(logits) || !ok_ptr(stats))
       return TPL_ERR_INVALID_ARG;
-    TPL_TRY(launch_gemm(gemm(m, true, true, m.N, m.vr, m.h, hidden, m.h, emb, m.h, logits, m.vr), s));
+    GemmDesc g = gemm(m, true, true, m.N, m.vr, m.h, hidden, m.h, emb, m.h, logits, m.vr);
+    const int tcols = xent_gemm_tile_cols(m.dt, m.N, m.vr);
+    if (tcols > 0) {
+      // statistics fused into the product's epilogue, per tile column, then
+      // merged per row; the tile statistics live behind the row statistics
+      g.epi = EPI_XENT;
+      g.targets = targets;
+      g.v0 = (int64_t)desc->rank * m.vr;
+      g.xpart = stats + xent_head_floats(m.N);
+      TPL_TRY(launch_gemm(g, s));
+      return from_hip(launch_xent_merge(m.dt, g.xpart, tcols, m.N, logits, m.vr, targets, g.v0, stats, s));
+    }
+    TPL_TRY(launch_gemm(g, s));
     return from_hip(launch_xent_stats(m.dt, logits, m.N, m.vr, targets, (int64_t)desc->rank * m.vr, stats, s));
   }
   if (phase != TPL_XENT_FINISH) return TPL_ERR_INVALID_ARG;

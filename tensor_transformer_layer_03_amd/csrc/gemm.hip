@@ -36,6 +36,9 @@ namespace {
 
 constexpr int kRowBytes = 128;   // one LDS row = one K-tile of one output row/col
 constexpr int kGroupM = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -47,6 +50,9 @@ struct Args {
   const char* bias;
   int M, N, K;
   int tiles_m, tiles_n;
+  const int32_t* targets;
+  int64_t v0;
+  float* xpart;
 };
 
 // Load a K-major operand tile (ROWS x BK) to registers: ROWS*8 chunks of 16 B.
@@ -664,6 +670,78 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   else static_assert(N < 0, "unsupported wait count");
 }
 
+// Fused cross-entropy statistics of a wave's TM x TN fragment block (rows
+// rb + 32i + lane%32, columns nb + ...): rounds to bf16 once, stores the
+// packed values, and writes per row (max, sum exp(l - max)) over the wave's
+// columns to xs[row within the tile]. FULL: every column is below N.
+template <int TM, int TN, bool FULL, int BM>
+__device__ __forceinline__ void xent_tile_stats(const Args& g, f32x16 (&acc)[TM][TN], float (&xs)[BM][2], int m0,
+                                                int nb, int rb, int lane) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int rt = rb + i * 32 + (lane & 31);
+    const int m = m0 + rt;
+    uint32_t pk[TN][8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const f32x2 pair = {acc[i][j][2 * h], acc[i][j][2 * h + 1]};
+        pk[j][h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, bf16x2));   // one v_cvt_pk_bf16_f32
+        const float x0 = __builtin_bit_cast(float, pk[j][h] << 16);
+        const float x1 = __builtin_bit_cast(float, pk[j][h] & 0xFFFF0000u);
+        if constexpr (FULL) {
+          mx = fmaxf(mx, fmaxf(x0, x1));
+        } else {
+          const int n = nb + j * 32 + 8 * (h >> 1) + 4 * (lane >> 5) + 2 * (h & 1);
+          if (n < g.N) mx = fmaxf(mx, x0);
+          if (n + 1 < g.N) mx = fmaxf(mx, x1);
+        }
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    float se = 0.f;
+    if (mx != -INFINITY) {
+      const float off = mx * kLog2e;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          // v_exp_f32 directly: arguments are <= 0 and results below the
+          // normal range are negligible in the sum
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(__builtin_bit_cast(float, pk[j][h] << 16), kLog2e, -off));
+          const float e1 =
+              __builtin_amdgcn_exp2f(fmaf(__builtin_bit_cast(float, pk[j][h] & 0xFFFF0000u), kLog2e, -off));
+          if constexpr (FULL) {
+            se += e0 + e1;
+          } else {
+            const int n = nb + j * 32 + 8 * (h >> 1) + 4 * (lane >> 5) + 2 * (h & 1);
+            if (n < g.N) se += e0;
+            if (n + 1 < g.N) se += e1;
+          }
+        }
+    }
+    se += __shfl_xor(se, 32, kWave);
+    if (lane < 32) {
+      xs[rt][0] = mx;
+      xs[rt][1] = se;
+    }
+    if (m < g.M) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nb + j * 32 + 8 * q + 4 * (lane >> 5);
+          if (FULL || n < g.N) {
+            u32x2 v = {pk[j][2 * q], pk[j][2 * q + 1]};
+            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16*>(g.C) + (int64_t)m * g.ldc + n) = v;
+          }
+        }
+    }
+  }
+}
+
+
 template <int BM, int BN, int WGM, int WGN, int NS, int OCC, int EPI, typename TC>
 __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_ms_kernel(Args g) {
   constexpr int NW = WGM * WGN;
@@ -781,6 +859,38 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
 #undef TPL_MS_ISSUE
 
+  if constexpr (EPI == EPI_XENT) {
+    // Logits tile (rounded once to bf16 and stored from the packed pairs)
+    // plus, per row, the statistics of its BN columns over the stored values:
+    // max and sum of exp(l - max). Lanes l and l^32 hold the two column halves
+    // of a row in a wave; the WGN waves of a row are merged through LDS in
+    // wave order. (The target logit is read back by the merge kernel.)
+    __shared__ float xs[WGN][BM][2];
+    if (n0 + BN <= g.N)
+      xent_tile_stats<TM, TN, true>(g, acc, xs[wn], m0, n0 + wn * WTN, wm * WTM, lane);
+    else
+      xent_tile_stats<TM, TN, false>(g, acc, xs[wn], m0, n0 + wn * WTN, wm * WTM, lane);
+    __syncthreads();
+    for (int rt = threadIdx.x; rt < BM; rt += NW * 64) {
+      const int m = m0 + rt;
+      if (m >= g.M) continue;
+      float M = xs[0][rt][0], S = xs[0][rt][1];
+#pragma unroll
+      for (int w = 1; w < WGN; ++w) {
+        const float m2 = xs[w][rt][0], s2 = xs[w][rt][1];
+        const float mn = fmaxf(M, m2);
+        if (mn != -INFINITY) {
+          S = S * __expf(M - mn) + s2 * __expf(m2 - mn);
+          M = mn;
+        }
+      }
+      float* o = g.xpart + ((int64_t)(n0 / BN) * g.M + m) * 2;
+      o[0] = M;
+      o[1] = S;
+    }
+    return;
+  }
+
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int m = m0 + wm * WTM + i * 32 + (lane & 31);
@@ -886,6 +996,7 @@ hipError_t run_ms(const GemmDesc& d, hipStream_t s) {
   a.M = (int)d.M; a.N = (int)d.N; a.K = (int)d.K;
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
+  a.targets = d.targets; a.v0 = d.v0; a.xpart = d.xpart;
   const int nblk = a.tiles_m * a.tiles_n;
   if (nblk == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_ms_kernel<BM, BN, WGM, WGN, NS, OCC, EPI, TC>), dim3(nblk), dim3(WGM * WGN * 64), 0, s, a);
@@ -922,6 +1033,13 @@ hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
       case EPI_NONE: return run_tiles<T, true, true, EPI_NONE, T>(d, s);
       case EPI_BIAS: return run_tiles<T, true, true, EPI_BIAS, T>(d, s);
       case EPI_BIAS_GELU: return run_tiles<T, true, true, EPI_BIAS_GELU, T>(d, s);
+      case EPI_XENT:
+        if constexpr (sizeof(T) == 2) {
+          if (xent_gemm_tile_cols(d.dtype, d.M, d.N) == (int)((d.N + 255) / 256))
+            return run_ms<256, 256, 2, 4, 4, 2, EPI_XENT, T>(d, s);
+          return run_ms<128, 128, 2, 2, 4, 2, EPI_XENT, T>(d, s);
+        }
+        return hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
   }
@@ -939,6 +1057,15 @@ hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
 }
 
 }  // namespace
+
+// The fused-statistics logits product uses the 256x256 four-stage tile when
+// that gives at least 384 workgroups, else its 128x128 form.
+int xent_gemm_tile_cols(int dtype, int64_t M, int64_t N) {
+  if (dtype != DT_BF16 || M <= 0 || N <= 0) return 0;
+  if (((M + 255) / 256) * ((N + 255) / 256) >= 384) return (int)((N + 255) / 256);
+  return (int)((N + 127) / 128);
+}
+size_t xent_part_floats(int64_t M, int64_t N) { return (size_t)((N + 127) / 128) * (size_t)M * 2; }
 
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
   TraceScope trace(d.a_kmajor && d.b_kmajor ? K_GEMM_NT : (d.a_kmajor ? K_GEMM_NN : K_GEMM_TN), s,

@@ -13,7 +13,7 @@ inline size_t dtype_size(int dt) { return dt == DT_BF16 ? 2 : 4; }
 enum KernelId {
   K_GEMM_NT = 0, K_GEMM_NN, K_GEMM_TN, K_ATTN_FWD, K_ATTN_BWD_PRE, K_ATTN_BWD_DQ,
   K_ATTN_BWD_DKDV, K_LN_FWD, K_LN_BWD, K_LN_BWD_COLS, K_COLSUM, K_COLSUM_FINAL,
-  K_PARTIAL_SUM, K_XENT_STATS, K_XENT_FINISH, K_XENT_DLOGITS, K_COUNT
+  K_PARTIAL_SUM, K_XENT_STATS, K_XENT_FINISH, K_XENT_DLOGITS, K_XENT_MERGE, K_COUNT
 };
 const char* kernel_name(int id);
 struct TraceScope {
@@ -29,7 +29,8 @@ enum Epilogue {
   EPI_NONE = 0,       // C = acc
   EPI_BIAS = 1,       // C = acc + bias[n]
   EPI_BIAS_GELU = 2,  // C = u = acc + bias[n]; C2 = GeLU(u)
-  EPI_DGELU = 3       // C = acc * GeLU'(C2[m][n])  (C2 holds u, read-only)
+  EPI_DGELU = 3,      // C = acc * GeLU'(C2[m][n])  (C2 holds u, read-only)
+  EPI_XENT = 4        // C = acc (logits); per-row (max, sum exp) of each tile column
 };
 struct GemmDesc {
   int dtype;          // storage type of A, B (and C unless c_f32)
@@ -43,8 +44,16 @@ struct GemmDesc {
   void* C; int64_t ldc;
   void* C2; int64_t ldc2;
   const void* bias;
+  // EPI_XENT only: targets [M] (global ids), v0 = first vocabulary id of the
+  // columns, xpart = per-tile (max, sum exp) [tile column][M][2]
+  const int32_t* targets; int64_t v0; float* xpart;
 };
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
+// Number of tile columns of the logits product with the fused statistics
+// epilogue (0: this shape/dtype takes the unfused path), and the floats of
+// per-tile statistics it needs at most.
+int xent_gemm_tile_cols(int dtype, int64_t M, int64_t N);
+size_t xent_part_floats(int64_t M, int64_t N);
 
 // ------------------------------------------------------------------ attention
 struct AttnDesc {
@@ -79,6 +88,10 @@ hipError_t launch_partial_sum(int dtype, const void* const* parts, int n, const 
                               hipStream_t s);
 
 // ------------------------------------------------------------------ cross-entropy
+// stats[row] = fixed-order log-sum-exp merge of the T tile (max, sum exp) pairs
+// of xpart [T][rows][2], and the target logit read from logits.
+hipError_t launch_xent_merge(int dtype, const float* xpart, int tcols, int64_t rows, const void* logits, int vr,
+                             const int32_t* targets, int64_t v0, float* stats, hipStream_t s);
 hipError_t launch_xent_stats(int dtype, const void* logits, int64_t rows, int vr,
                              const int32_t* targets, int64_t v0, float* stats, hipStream_t s);
 hipError_t launch_xent_finish(const float* const* all_stats, int t, int64_t rows,

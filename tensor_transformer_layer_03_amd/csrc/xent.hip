@@ -74,6 +74,41 @@ __global__ __launch_bounds__(256) void xent_stats_kernel(const T* __restrict__ l
   }
 }
 
+// stats[row] from the per-tile (max, sum exp) pairs of the fused logits
+// product: 64 rows per workgroup (lane = row), wave w of 16 merges the w-th
+// slice of the tile columns in order, then the slices are merged in order --
+// a fixed order, so the result is deterministic. The target logit is read
+// from the stored logits.
+template <typename T>
+__global__ __launch_bounds__(1024) void xent_merge_kernel(const float* __restrict__ xpart, int tcols, int64_t rows,
+                                                          const T* __restrict__ logits, int vr,
+                                                          const int32_t* __restrict__ targets, int64_t v0,
+                                                          float* __restrict__ stats) {
+  __shared__ float q[16][64][2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 64 + lane;
+  const int per = (tcols + 15) / 16;
+  const int t0 = wave * per, t1 = min(tcols, t0 + per);
+  float m = -INFINITY, s = 0.f;
+  if (row < rows) {
+    for (int t = t0; t < t1; ++t) {
+      const float2 p = *reinterpret_cast<const float2*>(xpart + ((int64_t)t * rows + row) * 2);
+      lse_merge(m, s, p.x, p.y);
+    }
+  }
+  q[wave][lane][0] = m;
+  q[wave][lane][1] = s;
+  __syncthreads();
+  if (wave == 0 && row < rows) {
+    float M = q[0][lane][0], S = q[0][lane][1];
+    for (int w = 1; w < 16; ++w) lse_merge(M, S, q[w][lane][0], q[w][lane][1]);
+    const int64_t t = (int64_t)targets[row] - v0;
+    stats[row * 3 + 0] = M;
+    stats[row * 3 + 1] = S;
+    stats[row * 3 + 2] = (t >= 0 && t < vr) ? to_f32(logits[row * vr + t]) : 0.f;
+  }
+}
+
 struct StatPtrs { const float* p[64]; };
 
 // Single workgroup: combine the t ranks' statistics, per-row loss and the
@@ -164,6 +199,19 @@ hipError_t launch_xent_stats(int dtype, const void* logits, int64_t rows, int vr
   else
     hipLaunchKernelGGL(xent_stats_kernel<float>, dim3((unsigned)rows), dim3(256), 0, s,
                        static_cast<const float*>(logits), vr, targets, v0, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_xent_merge(int dtype, const float* xpart, int tcols, int64_t rows, const void* logits, int vr,
+                             const int32_t* targets, int64_t v0, float* stats, hipStream_t s) {
+  TraceScope trace(K_XENT_MERGE, s, (double)rows * (8.0 * tcols + 12 + 6));
+  if (rows == 0) return hipSuccess;
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(xent_merge_kernel<bf16>, dim3((unsigned)((rows + 63) / 64)), dim3(1024), 0, s, xpart, tcols, rows,
+                       static_cast<const bf16*>(logits), vr, targets, v0, stats);
+  else
+    hipLaunchKernelGGL(xent_merge_kernel<float>, dim3((unsigned)((rows + 63) / 64)), dim3(1024), 0, s, xpart, tcols,
+                       rows, static_cast<const float*>(logits), vr, targets, v0, stats);
   return hipGetLastError();
 }
 

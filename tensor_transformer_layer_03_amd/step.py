@@ -102,20 +102,22 @@ class LayerStep:
             t = {k: _dev(v, dt, self.device) for k, v in hs.items()}
             sa = B.tp_layer_saved_bytes(desc, B.TPL_BLOCK_ATTN)
             sm = B.tp_layer_saved_bytes(desc, B.TPL_BLOCK_MLP)
-            if sa == 0 or sm == 0:
+            sx = B.vocab_parallel_xent_stats_bytes(desc)
+            if sa == 0 or sm == 0 or sx == 0:
                 raise ValueError(f"workload rejected by tp_layer_saved_bytes (rank {r})")
             f32 = torch.float32
             t.update({
                 "saved_attn": torch.empty(sa, dtype=torch.uint8, device=self.device),
                 "saved_mlp": torch.empty(sm, dtype=torch.uint8, device=self.device),
                 "part_attn": z(N, h), "part_mlp": z(N, h), "dln_attn": z(N, h), "dln_mlp": z(N, h),
-                "logits": z(N, vr), "stats": z(N, 3, dtype=f32), "dH": z(N, h),
+                "logits": z(N, vr), "stats_buf": z(sx // 4, dtype=f32), "dH": z(N, h),
                 "d_w_qkv": z(3 * hr, h, dtype=f32), "d_b_qkv": z(3 * hr, dtype=f32), "d_w_o": z(h, hr, dtype=f32),
                 "d_w_1": z(fr, h, dtype=f32), "d_b_1": z(fr, dtype=f32), "d_w_2": z(h, fr, dtype=f32),
                 "d_emb": z(vr, h, dtype=f32),
             })
             sh = self.shared
             attn = B.block_params(sh["ln1_g"], sh["ln1_b"], t["w_qkv"], t["b_qkv"], t["w_o"])
+            t["stats"] = t["stats_buf"][:N * 3].view(N, 3)   # the exchanged part; the rest is scratch
             mlp = B.block_params(sh["ln2_g"], sh["ln2_b"], t["w_1"], t["b_1"], t["w_2"])
             self.states.append(RankState(r, desc, attn, mlp, t))
         self.exchanges = 0
@@ -203,6 +205,6 @@ class LayerStep:
         out = {k: f(v) for k, v in self.shared.items() if k not in ("targets", "mask")}
         for st in self.states:
             for k, v in st.tensors.items():
-                if k.startswith(("d_", "part_", "dln_", "stats", "dH")):
+                if k.startswith(("d_", "part_", "dln_", "dH")) or k == "stats":
                     out[f"{k}@{st.rank}"] = f(v)
         return out
