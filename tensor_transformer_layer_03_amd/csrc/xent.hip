@@ -149,40 +149,42 @@ __global__ __launch_bounds__(1024) void xent_finish_kernel(StatPtrs st, int t, i
 }
 
 // In place: l <- g (exp(l - lse) - [j == target - v0]), g = dloss * mask / count.
-// Chunks are processed kU at a time (loads issued together) for bytes in flight.
+// Streams the [rows][vr] logits as one flat array of 16-B chunks (kU chunks
+// per thread, loads issued together); the per-row scalars are re-read per
+// chunk from cache.
 template <typename T>
-__global__ __launch_bounds__(256) void xent_dlogits_kernel(T* logits, int vr, const int32_t* __restrict__ targets,
-                                                           int64_t v0, const uint8_t* __restrict__ mask,
+__global__ __launch_bounds__(256) void xent_dlogits_kernel(T* logits, int vr, int64_t nchunks,
+                                                           const int32_t* __restrict__ targets, int64_t v0,
+                                                           const uint8_t* __restrict__ mask,
                                                            const float* __restrict__ lse,
                                                            const float* __restrict__ loss, float dloss) {
   constexpr int V = Vec16<T>::N, kU = 4;
-  const int64_t row = blockIdx.x;
-  T* lr = logits + row * vr;
-  const int nch = vr / V;
+  const int cpr = vr / V;   // chunks per row
   const float cnt = loss[1];
-  const float g = (mask ? (float)mask[row] : 1.f) * (cnt > 0.f ? dloss / cnt : 0.f);
-  const float L = lse[row];
-  const int64_t t = (int64_t)targets[row] - v0;
-  for (int base = threadIdx.x; base < nch; base += 256 * kU) {
-    Vec16<T> x[kU];
+  const float gs = cnt > 0.f ? dloss / cnt : 0.f;
+  const int64_t base = ((int64_t)blockIdx.x * kU) * 256 + threadIdx.x;
+  Vec16<T> x[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int ch = base + 256 * u;
-      if (ch < nch) x[u].raw = ld16(lr + ch * V);
-    }
+  for (int u = 0; u < kU; ++u) {
+    const int64_t c = base + 256 * u;
+    if (c < nchunks) x[u].raw = ld16(logits + c * V);
+  }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int ch = base + 256 * u;
-      if (ch < nch) {
+  for (int u = 0; u < kU; ++u) {
+    const int64_t c = base + 256 * u;
+    if (c < nchunks) {
+      const uint32_t row = (uint32_t)c / (uint32_t)cpr;   // nchunks < 2^32 (checked by the launcher)
+      const int j0 = (int)((uint32_t)c - row * (uint32_t)cpr) * V;
+      const float g = (mask ? (float)mask[row] : 1.f) * gs;
+      const float L = lse[row];
+      const int64_t t = (int64_t)targets[row] - v0 - j0;
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const int j = ch * V + e;
-          float p = __expf(to_f32(x[u].get(e)) - L);
-          if (j == t) p -= 1.f;
-          x[u].set(e, from_f32<T>(g * p));
-        }
-        st16(lr + ch * V, x[u].raw);
+      for (int e = 0; e < V; ++e) {
+        float p = __expf(to_f32(x[u].get(e)) - L);
+        if (e == t) p -= 1.f;
+        x[u].set(e, from_f32<T>(g * p));
       }
+      st16(logits + c * V, x[u].raw);
     }
   }
 }
@@ -228,12 +230,16 @@ hipError_t launch_xent_dlogits(int dtype, void* logits, int64_t rows, int vr, co
                                const uint8_t* mask, const float* lse, const float* loss, float dloss, hipStream_t s) {
   TraceScope trace(K_XENT_DLOGITS, s, (double)rows * vr * 2 * dtype_size(dtype) + rows * 9.0);
   if (rows == 0) return hipSuccess;
+  const int v = dtype == DT_BF16 ? 8 : 4;
+  const int64_t nchunks = rows * (vr / v);
+  if (nchunks >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((nchunks + 1023) / 1024));
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL(xent_dlogits_kernel<bf16>, dim3((unsigned)rows), dim3(256), 0, s, static_cast<bf16*>(logits),
-                       vr, targets, v0, mask, lse, loss, dloss);
+    hipLaunchKernelGGL(xent_dlogits_kernel<bf16>, grid, dim3(256), 0, s, static_cast<bf16*>(logits), vr, nchunks,
+                       targets, v0, mask, lse, loss, dloss);
   else
-    hipLaunchKernelGGL(xent_dlogits_kernel<float>, dim3((unsigned)rows), dim3(256), 0, s,
-                       static_cast<float*>(logits), vr, targets, v0, mask, lse, loss, dloss);
+    hipLaunchKernelGGL(xent_dlogits_kernel<float>, grid, dim3(256), 0, s, static_cast<float*>(logits), vr, nchunks,
+                       targets, v0, mask, lse, loss, dloss);
   return hipGetLastError();
 }
 
