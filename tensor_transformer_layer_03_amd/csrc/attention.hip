@@ -158,8 +158,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) T sVt[2][D * VT::kLd];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
-  const int qb = gridDim.x - 1 - blockIdx.x;   // heaviest causal blocks first
-  const int b = blockIdx.y / a.heads, hd = blockIdx.y % a.heads;
+  // 1-D grid dealt heaviest query tiles first over all heads (causal tiles
+  // differ up to seq/BQ-fold in work, so the last to start are the short ones)
+  const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs;
+  const int qb = gridDim.x / bhs - 1 - blockIdx.x / bhs;
+  const int b = bh / a.heads, hd = bh % a.heads;
   const int s = a.seq;
   const int hr = a.heads * D;
   const T* Qg = reinterpret_cast<const T*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
@@ -306,8 +309,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) T sKt[2][D * TT::kLd];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
-  const int qb = gridDim.x - 1 - blockIdx.x;
-  const int b = blockIdx.y / a.heads, hd = blockIdx.y % a.heads;
+  // 1-D grid dealt heaviest query tiles first over all heads (causal tiles
+  // differ up to seq/BQ-fold in work, so the last to start are the short ones)
+  const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs;
+  const int qb = gridDim.x / bhs - 1 - blockIdx.x / bhs;
+  const int b = bh / a.heads, hd = bh % a.heads;
   const int s = a.seq, hr = a.heads * D;
   const T* Qg = reinterpret_cast<const T*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
   const T* Kg = Qg + hr;
@@ -420,14 +426,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) float sDl[2][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
-  const int b = blockIdx.y / a.heads, hd = blockIdx.y % a.heads;
+  // 1-D grid dealt heaviest key tiles (the first ones, under a causal mask) first over all heads
+  const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs, kb = blockIdx.x / bhs;
+  const int b = bh / a.heads, hd = bh % a.heads;
   const int s = a.seq, hr = a.heads * D;
   const T* Qg = reinterpret_cast<const T*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
   const T* Kg = Qg + hr;
   const T* Vg = Qg + 2 * hr;
   const T* dOg = reinterpret_cast<const T*>(a.dctx) + (int64_t)b * s * a.ld_ctx + hd * D;
   const int64_t stat = ((int64_t)b * a.heads + hd) * s;
-  const int k0 = blockIdx.x * BKB, k0w = k0 + wave * 32, my_k = k0w + l32;
+  const int k0 = kb * BKB, k0w = k0 + wave * 32, my_k = k0w + l32;
   const float c = kLog2e * rsqrtf((float)D);
 
   Frag8<T> kf[D / 16], vf[D / 16];
@@ -613,8 +621,11 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char sV[2][Tile::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
-  const int qb = gridDim.x - 1 - blockIdx.x;   // heaviest causal blocks first
-  const int b = blockIdx.y / a.heads, hd = blockIdx.y % a.heads;
+  // 1-D grid dealt heaviest query tiles first over all heads (causal tiles
+  // differ up to seq/BQ-fold in work, so the last to start are the short ones)
+  const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs;
+  const int qb = gridDim.x / bhs - 1 - blockIdx.x / bhs;
+  const int b = bh / a.heads, hd = bh % a.heads;
   const int s = a.seq, hr = a.heads * D;
   const bf16* Qg = reinterpret_cast<const bf16*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
   const bf16* Kg = Qg + hr;
@@ -735,8 +746,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char sV[2][Tile::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
-  const int qb = gridDim.x - 1 - blockIdx.x;
-  const int b = blockIdx.y / a.heads, hd = blockIdx.y % a.heads;
+  // 1-D grid dealt heaviest query tiles first over all heads (causal tiles
+  // differ up to seq/BQ-fold in work, so the last to start are the short ones)
+  const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs;
+  const int qb = gridDim.x / bhs - 1 - blockIdx.x / bhs;
+  const int b = bh / a.heads, hd = bh % a.heads;
   const int s = a.seq, hr = a.heads * D;
   const bf16* Qg = reinterpret_cast<const bf16*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
   const bf16* Kg = Qg + hr;
@@ -835,7 +849,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(Args a) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(Args a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void attn_bwd_dkdv_bf16_kernel(Args a) {
   constexpr int NT = 256, BKB = 128, BQ = 64;
   using Tile = NatTile<D, NT>;
   __shared__ __attribute__((aligned(16))) char sQ[2][Tile::kBytes];
@@ -844,14 +858,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) float sDl[2][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
-  const int b = blockIdx.y / a.heads, hd = blockIdx.y % a.heads;
+  // 1-D grid dealt heaviest key tiles (the first ones, under a causal mask) first over all heads
+  const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs, kb = blockIdx.x / bhs;
+  const int b = bh / a.heads, hd = bh % a.heads;
   const int s = a.seq, hr = a.heads * D;
   const bf16* Qg = reinterpret_cast<const bf16*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
   const bf16* Kg = Qg + hr;
   const bf16* Vg = Qg + 2 * hr;
   const bf16* dOg = reinterpret_cast<const bf16*>(a.dctx) + (int64_t)b * s * a.ld_ctx + hd * D;
   const int64_t stat = ((int64_t)b * a.heads + hd) * s;
-  const int k0 = blockIdx.x * BKB, k0w = k0 + wave * 32, my_k = k0w + l32;
+  const int k0 = kb * BKB, k0w = k0 + wave * 32, my_k = k0w + l32;
   const float c = kLog2e * rsqrtf((float)D);
   const int qrow = swap23(l32);
 
@@ -985,7 +1001,7 @@ Args make_args(const AttnDesc& d) {
 template <typename T, int D>
 hipError_t fwd_t(const AttnDesc& d, hipStream_t s) {
   Args a = make_args(d);
-  dim3 grid((d.seq + 127) / 128, d.batch * d.heads);
+  dim3 grid((unsigned)(((d.seq + 127) / 128) * d.batch * d.heads));
   if constexpr (sizeof(T) == 2) {
     if (d.causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), grid, dim3(256), 0, s, a);
@@ -1006,7 +1022,7 @@ hipError_t bwd_t(const AttnDesc& d, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  dim3 grid((d.seq + 127) / 128, d.batch * d.heads);
+  dim3 grid((unsigned)(((d.seq + 127) / 128) * d.batch * d.heads));
   {
     TraceScope trace(K_ATTN_BWD_DKDV, s, 6.0 * attn_pairs(d) * d.head_dim);   // dV, dP, dK
     if constexpr (sizeof(T) == 2) {
