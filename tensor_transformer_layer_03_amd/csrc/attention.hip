@@ -614,7 +614,7 @@ struct NatTile {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(Args a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attn_fwd_bf16_kernel(Args a) {
   constexpr int NT = 256, BQ = 128, BKV = 64;
   using Tile = NatTile<D, NT>;
   __shared__ __attribute__((aligned(16))) char sK[2][Tile::kBytes];
