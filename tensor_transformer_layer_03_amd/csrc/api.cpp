@@ -98,11 +98,15 @@ Saved saved_layout(const Dims& m, tpl_block block) {
     sz[S_DQKV] = m.N * 3 * m.hr * es;
     sz[S_DELTA] = m.N * m.heads_r * 4;
     ws = std::max(ws, colsum_ws_floats(m.N, 3 * m.hr));
+    ws = std::max(ws, gemm_ws_floats(m.dt, m.h, m.hr, m.N));       // dW_o
+    ws = std::max(ws, gemm_ws_floats(m.dt, 3 * m.hr, m.h, m.N));   // dW_qkv
   } else {
     sz[S_U] = m.N * m.fr * es;
     sz[S_ACT] = m.N * m.fr * es;
     sz[S_DU] = m.N * m.fr * es;
     ws = std::max(ws, colsum_ws_floats(m.N, m.fr));
+    ws = std::max(ws, gemm_ws_floats(m.dt, m.h, m.fr, m.N));       // dW_2
+    ws = std::max(ws, gemm_ws_floats(m.dt, m.fr, m.h, m.N));       // dW_1
   }
   sz[S_WS] = ws * 4;
   size_t at = 0;
@@ -314,6 +318,7 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     TPL_TRY(launch_gemm(gemm(m, true, false, m.N, m.hr, m.h, dy, m.h, p->w_out, m.hr, dctx, m.hr), s));
     GemmDesc gw = gemm(m, false, false, m.h, m.hr, m.N, dy, m.h, ctx, m.hr, gr->d_w_out, m.hr);
     gw.c_f32 = true;
+    gw.ws = ws;
     TPL_TRY(launch_gemm(gw, s));
     AttnDesc a{};
     a.dtype = m.dt; a.batch = desc->micro_batch; a.heads = m.heads_r; a.seq = desc->seq;
@@ -325,6 +330,7 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     // dW_qkv = dqkv^T y ; db_qkv = colsum(dqkv) ; d_ln = dqkv W_qkv
     GemmDesc gq = gemm(m, false, false, 3 * m.hr, m.h, m.N, dqkv, 3 * m.hr, y, m.h, gr->d_w_in, m.h);
     gq.c_f32 = true;
+    gq.ws = ws;
     TPL_TRY(launch_gemm(gq, s));
     TPL_TRY(launch_colsum(m.dt, dqkv, 3 * m.hr, m.N, 3 * m.hr, gr->d_b_in, ws, s));
     TPL_TRY(launch_gemm(gemm(m, true, false, m.N, m.h, 3 * m.hr, dqkv, 3 * m.hr, p->w_in, m.h, d_ln_partial, m.h), s));
@@ -340,9 +346,11 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     TPL_TRY(launch_gemm(g, s));
     GemmDesc g2 = gemm(m, false, false, m.h, m.fr, m.N, dy, m.h, act, m.fr, gr->d_w_out, m.fr);
     g2.c_f32 = true;
+    g2.ws = ws;
     TPL_TRY(launch_gemm(g2, s));
     GemmDesc g1 = gemm(m, false, false, m.fr, m.h, m.N, du, m.fr, y, m.h, gr->d_w_in, m.h);
     g1.c_f32 = true;
+    g1.ws = ws;
     TPL_TRY(launch_gemm(g1, s));
     TPL_TRY(launch_colsum(m.dt, du, m.fr, m.N, m.fr, gr->d_b_in, ws, s));
     TPL_TRY(launch_gemm(gemm(m, true, false, m.N, m.h, m.fr, du, m.fr, p->w_in, m.h, d_ln_partial, m.h), s));

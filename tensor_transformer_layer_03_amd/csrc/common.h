@@ -120,9 +120,29 @@ __device__ __forceinline__ void frag_from_f32(Frag8<float>& f, const float* v) {
 // ---------------------------------------------------------------- math
 
 // Exact GeLU x*Phi(x) and its derivative Phi(x) + x*phi(x).
-__device__ __forceinline__ float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// Exact-erf GeLU (u * Phi(u)) and its derivative Phi(u) + u * phi(u), with the
+// normal CDF from the complementary error function of Abramowitz & Stegun,
+// Handbook of Mathematical Functions, 7.1.26: erfc(x) = t (a1 + t (a2 + ...))
+// e^{-x^2}, t = 1 / (1 + p x), x >= 0, absolute error <= 1.5e-7. Taking erfc
+// of |u| / sqrt(2) keeps the left tail free of cancellation, and e^{-u^2/2}
+// is shared with the density.
+__device__ __forceinline__ float normal_cdf_tail(float u, float& gauss) {
+  const float x = fabsf(u) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f), 0.254829592f);
+  gauss = __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);   // e^{-u^2/2}; underflows to 0 in the far tail
+  const float half_erfc = 0.5f * poly * gauss;
+  return u >= 0.0f ? 1.0f - half_erfc : half_erfc;                 // Phi(u)
+}
+__device__ __forceinline__ float gelu_f(float x) {
+  float g;
+  return x * normal_cdf_tail(x, g);
+}
 __device__ __forceinline__ float gelu_grad_f(float x) {
-  return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * 0.39894228040143268f * __expf(-0.5f * x * x);
+  float g;
+  const float cdf = normal_cdf_tail(x, g);
+  return fmaf(x * 0.39894228040143268f, g, cdf);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -53,6 +53,8 @@ struct Args {
   const int32_t* targets;
   int64_t v0;
   float* xpart;
+  float* ws;       // split-K partials [splits-1][M][N] (split 0 writes C)
+  int splits, kchunk;
 };
 
 // Load a K-major operand tile (ROWS x BK) to registers: ROWS*8 chunks of 16 B.
@@ -469,7 +471,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
   const int wm = wave % WGM, wn = wave / WGM;
 
   const int nblk = g.tiles_m * g.tiles_n;
-  const int bid = blockIdx.x;
+  int bid = blockIdx.x;
+  if (g.splits > 1) {
+    // split-K: workgroup (split, tile) takes K range [split*kchunk, ...);
+    // split 0 writes C, split s the workspace slice s-1 (summed afterwards
+    // in split order)
+    const int split = bid / nblk;
+    bid -= split * nblk;
+    const int kb = split * g.kchunk;
+    g.A += A_K ? (int64_t)kb * 2 : (int64_t)kb * g.lda * 2;
+    g.B += B_K ? (int64_t)kb * 2 : (int64_t)kb * g.ldb * 2;
+    g.K = min(g.kchunk, g.K - kb);
+    if (split > 0) {
+      g.C = reinterpret_cast<char*>(g.ws + (int64_t)(split - 1) * g.M * g.N);
+      g.ldc = g.N;
+    }
+  }
   const int xcd = bid & 7, local = bid >> 3;
   const int per = nblk >> 3, rem = nblk & 7;
   const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
@@ -918,6 +935,40 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
+// ------------------------------------------------------------------ split-K sum
+// C[m][n] += ws[0][m][n] + ws[1][m][n] + ... in split order (deterministic).
+__global__ __launch_bounds__(256) void splitk_sum_kernel(float* C, int64_t ldc, const float* __restrict__ ws,
+                                                         int nsum, int M, int N) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (int64_t)M * N) return;
+  const int64_t m = i / N, n = i % N;
+  float* c = C + m * ldc + n;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(c);
+  for (int sp = 0; sp < nsum; ++sp) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(ws + (int64_t)sp * M * N + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += v[e];
+  }
+  *reinterpret_cast<f32x4*>(c) = acc;
+}
+
+// Split of a weight-gradient product (both operands MN-major, fp32 output)
+// that takes the 128x128 tile: enough splits to put about two workgroups on
+// every CU, each split at least 1024 deep in K.
+struct SplitK { int splits, kchunk; };
+SplitK splitk_for(int dtype, int64_t M, int64_t N, int64_t K) {
+  SplitK r{1, (int)K};
+  if (dtype != DT_BF16 || getenv("TPL_GEMM_TILE")) return r;
+  if (((M + 255) / 256) * ((N + 255) / 256) >= 384) return r;   // 256x256 tile, enough workgroups
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int64_t sp = std::min<int64_t>(K / 1024, 512 / std::max<int64_t>(tiles, 1));
+  if (sp < 2) return r;
+  const int64_t chunk = ((K + sp - 1) / sp + 63) / 64 * 64;
+  r.splits = (int)((K + chunk - 1) / chunk);
+  r.kchunk = (int)chunk;
+  return r;
+}
+
 // ------------------------------------------------------------------ dispatch
 
 struct TileCfg { int bm, bn, variant; };
@@ -978,10 +1029,25 @@ hipError_t run_v2(const GemmDesc& d, hipStream_t s) {
   a.M = (int)d.M; a.N = (int)d.N; a.K = (int)d.K;
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
+  a.splits = 1;
+  a.kchunk = a.K;
+  a.ws = nullptr;
+  if (!AK && !BK_ && d.c_f32 && d.ws && BM == 128 && BN == 128) {
+    const SplitK sk = splitk_for(d.dtype, d.M, d.N, d.K);
+    a.splits = sk.splits;
+    a.kchunk = sk.kchunk;
+    a.ws = d.ws;
+  }
   const int nblk = a.tiles_m * a.tiles_n;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, AK, BK_, kDma, EPI, TC>), dim3(nblk), dim3(WGM * WGN * 64), 0,
-                     s, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, AK, BK_, kDma, EPI, TC>), dim3(nblk * a.splits),
+                     dim3(WGM * WGN * 64), 0, s, a);
+  if (a.splits > 1) {
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    const int64_t quads = (d.M * d.N + 3) / 4;
+    hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
+                       static_cast<float*>(d.C), d.ldc, d.ws, a.splits - 1, a.M, a.N);
+  }
   return hipGetLastError();
 }
 
@@ -1064,6 +1130,10 @@ int xent_gemm_tile_cols(int dtype, int64_t M, int64_t N) {
   if (dtype != DT_BF16 || M <= 0 || N <= 0) return 0;
   if (((M + 255) / 256) * ((N + 255) / 256) >= 384) return (int)((N + 255) / 256);
   return (int)((N + 127) / 128);
+}
+size_t gemm_ws_floats(int dtype, int64_t M, int64_t N, int64_t K) {
+  const SplitK sk = splitk_for(dtype, M, N, K);
+  return sk.splits > 1 ? (size_t)(sk.splits - 1) * (size_t)M * (size_t)N : 0;
 }
 size_t xent_part_floats(int64_t M, int64_t N) { return (size_t)((N + 127) / 128) * (size_t)M * 2; }
 

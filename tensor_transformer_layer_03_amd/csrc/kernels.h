@@ -44,11 +44,16 @@ struct GemmDesc {
   void* C; int64_t ldc;
   void* C2; int64_t ldc2;
   const void* bias;
+  // split-K workspace for fp32 outputs (or NULL: never split); see gemm_ws_floats
+  float* ws;
   // EPI_XENT only: targets [M] (global ids), v0 = first vocabulary id of the
   // columns, xpart = per-tile (max, sum exp) [tile column][M][2]
   const int32_t* targets; int64_t v0; float* xpart;
 };
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
+// Floats of split-K workspace the product (M, N, K) with both operands MN-major
+// and an fp32 output takes (0: it is not split).
+size_t gemm_ws_floats(int dtype, int64_t M, int64_t N, int64_t K);
 // Number of tile columns of the logits product with the fused statistics
 // epilogue (0: this shape/dtype takes the unfused path), and the floats of
 // per-tile statistics it needs at most.
