@@ -173,15 +173,30 @@ def kernel_family(name: str) -> str:
             flags = [f == "1" for f in re.findall(r"Lb([01])E", name)]
         ak, bk = (flags + [True, True])[:2]
         return "gemm_nt" if ak and bk else ("gemm_nn" if ak else "gemm_tn")
+    if "splitk_sum" in name:          # the split-K sum is part of the weight-gradient product's launch
+        return "gemm_tn"
+    if "colpart" in name:             # LN-gradient (3 outputs) or bias-gradient (1 output) column partials
+        if "Li3E" in name or ", 3>" in name:
+            return "layernorm_bwd_cols"
+        if "Li1E" in name or ", 1>" in name:
+            return "colsum"
+        return "colpart"
     table = [("attn_bwd_dkdv", "attn_bwd_dkdv"), ("attn_bwd_dq", "attn_bwd_dq"), ("attn_bwd_pre", "attn_bwd_pre"),
              ("attn_fwd", "attn_fwd"), ("ln_bwd_cols", "layernorm_bwd_cols"), ("ln_bwd", "layernorm_bwd"),
              ("ln_fwd", "layernorm_fwd"), ("colsum_final", "colsum_final"), ("colsum", "colsum"),
              ("partial_sum", "partial_sum"), ("xent_stats", "xent_stats"), ("xent_finish", "xent_finish"),
-             ("xent_dlogits", "xent_dlogits")]
+             ("xent_dlogits", "xent_dlogits"), ("xent_merge", "xent_merge")]
     for key, fam in table:
         if key in name:
             return fam
     return "other"
+
+
+def attached(name: str) -> bool:
+    """Dispatches that belong to the preceding launch of their family (the
+    split-K sum of a weight-gradient product): their time and bytes count,
+    their dispatch does not count as a launch."""
+    return "splitk_sum" in name
 
 
 def source_sha(family: str) -> str:
@@ -203,13 +218,14 @@ def summarize_profiles(d: str, workload: str):
     fam = collections.defaultdict(lambda: [0, 0.0])
     for r in rows:
         f = kernel_family(r["Name"])
-        fam[f][0] += int(r["Calls"])
+        fam[f][0] += 0 if attached(r["Name"]) else int(r["Calls"])
         fam[f][1] += float(r["TotalDurationNs"])
     total = sum(v[1] for v in fam.values())
     lines = [f"# Kernel time, {workload} (rocprofv3 --kernel-trace --stats)", "",
              "Command (repo root = <repo>, output dir = <out>):", "", "    " + PROFILE_CMDS["trace"], "",
              "Every launch of the run (warm-up, timed and traced steps); all are whole passes, so the mix per",
-             "kernel family is the same as in one step.", "",
+             "kernel family is the same as in one step. A weight-gradient product's split-K sum is counted",
+             "in its launch (gemm_tn), as the library's own launch timing does.", "",
              "| family | launches | total ms | avg us | share |", "|---|---|---|---|---|"]
     for f, (c, t) in sorted(fam.items(), key=lambda kv: -kv[1][1]):
         lines.append(f"| {f} | {c} | {t / 1e6:.3f} | {t / c / 1e3:.1f} | {100 * t / total:.1f}% |")
@@ -226,10 +242,13 @@ def summarize_profiles(d: str, workload: str):
         cp = [float(r["Counter_Value"]) for r in csv.DictReader(open(os.path.join(d, f"pmc_{c}", "copy_counter_collection.csv")))
               if "copyBuffer" in r["Kernel_Name"]]
         scale[c] = copy_bytes / (sorted(cp)[len(cp) // 2] * 1024)
-        acc = collections.defaultdict(list)
+        tot = collections.defaultdict(float)
+        cnt = collections.defaultdict(int)
         for r in csv.DictReader(open(os.path.join(d, f"pmc_{c}", "bench_counter_collection.csv"))):
-            acc[kernel_family(r["Kernel_Name"])].append(float(r["Counter_Value"]) * 1024 * scale[c])
-        per[c] = {k: sum(v) / len(v) for k, v in acc.items()}
+            f = kernel_family(r["Kernel_Name"])
+            tot[f] += float(r["Counter_Value"]) * 1024 * scale[c]
+            cnt[f] += 0 if attached(r["Kernel_Name"]) else 1
+        per[c] = {k: tot[k] / max(cnt[k], 1) for k in tot}
     traffic = {f: {"fetch_bytes_per_launch": per["FETCH_SIZE"].get(f, 0.0),
                    "write_bytes_per_launch": per["WRITE_SIZE"].get(f, 0.0),
                    "bytes_per_launch": per["FETCH_SIZE"].get(f, 0.0) + per["WRITE_SIZE"].get(f, 0.0),

@@ -7,22 +7,24 @@
 // (guide page section 1.2: tensor parallelism splits one matrix product over
 // devices; each rank runs its slice through this kernel.)
 //
-// Design:
-//  * workgroup tile BM x BN, K-tile of 128 bytes per row (64 bf16 / 32 fp32),
-//    two LDS buffers (one barrier per K-tile), the next K-tile prefetched into
-//    registers while MFMAs consume the current one;
-//  * LDS rows are 128 B = 8 chunks of 16 B, chunk c of row r stored at
-//    c ^ ((r ^ r>>3) & 7) so that fragment reads (32 consecutive rows, one
-//    chunk) and transposed writes (rows 8 apart) are bank-conflict free;
-//  * MN-major operands are loaded as 8 k-rows x 16 B, transposed in registers
-//    and written K-contiguous, so the MFMA loop is identical for all layouts;
-//  * the wave tile is a grid of 32x32 outputs, each a v_mfma_f32_32x32x16_bf16
-//    per 16 k (fp32: 8 x v_mfma_f32_32x32x2f32). The weight-side fragment is
-//    the MFMA's A operand, so lane l owns output row m = l%32 and four
-//    consecutive columns per accumulator quad: epilogue stores are 8/16 B;
-//  * workgroups are renumbered so that consecutive tiles share an XCD (the
-//    dispatcher deals workgroups to the 8 XCDs round-robin, each with its own
-//    L2), then walked in groups of GROUP_M tile-rows for L2 reuse of B.
+// Kernels (all on v_mfma_f32_32x32x16_bf16 per 16 k; fp32: 8 x
+// v_mfma_f32_32x32x2f32). The weight-side fragment is the MFMA's A operand,
+// so lane l owns output row m = l%32 and four consecutive columns per
+// accumulator quad: epilogue stores are 8/16 B.
+//  * gemm_kernel (fp32 storage): 128x128 tile, K-tile of 32 fp32 (128-B LDS
+//    rows), MN-major operands loaded as 8 k-rows x 16 B and transposed across
+//    lanes before the K-contiguous LDS store;
+//  * gemm_bf16_kernel: 256x256 (8 waves) or 128x128 (4 waves) tile, K-tile of
+//    64 bf16, two LDS stages; forward operands go straight to LDS
+//    (buffer_load ... lds), MN-major operands through registers into an
+//    [k][mn] LDS tile read with ds_read_b64_tr_b16; optional deterministic
+//    split-K for fp32 weight gradients;
+//  * gemm_ms_kernel (forward products only): K-tile of 32 bf16, four LDS
+//    stages fed three tiles ahead, with the fused loss-statistics epilogue
+//    for the logits.
+// Workgroups are renumbered so that consecutive tiles share an XCD (the
+// dispatcher deals workgroups to the 8 XCDs round-robin, each with its own
+// L2), then walked in groups of kGroupM tile-rows for L2 reuse of B.
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
