@@ -306,6 +306,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, n, 0x00020000);
 }
 
+// LDS layout of direct-to-LDS K-major tiles ("padded"): 1 KB blocks of 8
+// rows x 128 B at a pitch of 1040 B; block b holds rows b%8 + 8p + 64(b/8),
+// p = 0..7, at position p, each row's 8 chunks in natural order. A load
+// instruction then reads 8 whole 128-B lines in order (one 128-B request per
+// line instead of two 64-B ones), and a fragment read of 16 consecutive rows
+// at one chunk still lands on 16 distinct 16-B bank groups: row R sits at
+// (R%8) * 1040 + ((R/8)%2) * 128 modulo 256.
+constexpr int kPadBlk = 1040;
+template <int ROWS, bool PAD>
+constexpr int tile_bytes() { return PAD ? ROWS / 8 * kPadBlk : ROWS * 128; }
+__device__ __forceinline__ int pad_row_off(int r) { return ((r & 7) + 8 * (r >> 6)) * kPadBlk + ((r >> 3) & 7) * 128; }
+
 // Direct-to-LDS loads of one operand tile (ROWS x 64 bf16) for one wave:
 // kInst instructions of 1 KB; per-lane byte offsets are fixed over K.
 template <int ROWS, bool KMAJ, int NW>
@@ -319,9 +331,9 @@ struct TileDma {
 #pragma unroll
     for (int j = 0; j < kInst; ++j) {
       const int blk = j * NW + wave;
-      if constexpr (KMAJ) {
-        const int r = blk * 8 + (lane >> 3);
-        voff[j] = (int)(((int64_t)r * ld + (((lane & 7) ^ swz_k(r)) * 8)) * 2);
+      if constexpr (KMAJ) {   // padded layout: block blk, position lane/8, chunk lane%8
+        const int r = (blk & 7) + 8 * (lane >> 3) + 64 * (blk >> 3);
+        voff[j] = (int)(((int64_t)r * ld + (lane & 7) * 8) * 2);
       } else {
         constexpr int kChunks = ROWS / 8, kRowsPerBlk = 64 / kChunks;
         const int k = blk * kRowsPerBlk + lane / kChunks;
@@ -337,7 +349,8 @@ struct TileDma {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
 #pragma unroll
     for (int j = 0; j < kInst; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (j * NW + wave) * 1024), 16, voff[j], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (j * NW + wave) * (KMAJ ? kPadBlk : 1024)), 16,
+                                               voff[j], soff, 0, 0);
 #endif
   }
 };
@@ -399,7 +412,7 @@ struct TileReg {
   do {                                                             \
     if constexpr (DMA) {                                           \
       tA.issue(TPL_TILE_ARGS_A(KT_), (S_), wave);                  \
-      tB.issue(TPL_TILE_ARGS_B(KT_), (S_) + BM * 128, wave);       \
+      tB.issue(TPL_TILE_ARGS_B(KT_), (S_) + kBOff, wave);          \
     } else {                                                       \
       tA.load(TPL_TILE_ARGS_A(KT_));                               \
       tB.load(TPL_TILE_ARGS_B(KT_));                               \
@@ -407,9 +420,12 @@ struct TileReg {
   } while (0)
 
 // Fragment of tile row r0 + lane%32, k-slots 8*(lane/32)..+7 of step st.
-template <int ROWS, bool KMAJ>
+template <int ROWS, bool KMAJ, bool PAD>
 __device__ __forceinline__ void frag_v2(Frag8<bf16>& f, const char* tile, int r0, int st, int lane) {
-  if constexpr (KMAJ) {
+  if constexpr (KMAJ && PAD) {
+    const int r = r0 + (lane & 31);
+    load_frag(f, reinterpret_cast<const bf16*>(tile + pad_row_off(r) + (2 * st + (lane >> 5)) * 16));
+  } else if constexpr (KMAJ) {
     const int r = r0 + (lane & 31);
     const int c = (2 * st + (lane >> 5)) ^ swz_k(r);
     load_frag(f, reinterpret_cast<const bf16*>(tile + r * 128 + c * 16));
@@ -428,13 +444,13 @@ __device__ __forceinline__ void frag_v2(Frag8<bf16>& f, const char* tile, int r0
 }
 
 // Fragments of step st for a wave's TM row tiles (A) and TN column tiles (B).
-template <int BM, int BN, bool A_K, bool B_K, int TM, int TN>
+template <int BM, int BN, bool A_K, bool B_K, bool PAD, int TM, int TN>
 __device__ __forceinline__ void read_frags(Frag8<bf16> (&fa)[TM], Frag8<bf16> (&fb)[TN], const char* stage, int st,
                                            int arow, int brow, int lane) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) frag_v2<BM, A_K>(fa[i], stage, arow + i * 32, st, lane);
+  for (int i = 0; i < TM; ++i) frag_v2<BM, A_K, PAD>(fa[i], stage, arow + i * 32, st, lane);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) frag_v2<BN, B_K>(fb[j], stage + BM * 128, brow + j * 32, st, lane);
+  for (int j = 0; j < TN; ++j) frag_v2<BN, B_K, PAD>(fb[j], stage + tile_bytes<BM, PAD>(), brow + j * 32, st, lane);
 }
 
 template <int TM, int TN>
@@ -461,11 +477,48 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
 
+// Output tile staged through LDS: the waves write their values (4
+// consecutive columns per lane and accumulator quad) into an LDS copy of the
+// tile's rows, 16-B chunks XOR-swizzled by row; then every thread copies whole
+// 16-B chunks of whole rows to global memory, so a wave's store covers full
+// 128-B lines (a direct store from the MFMA layout touches 32 rows with 16 B
+// each, and the memory pipeline pays per line).
+template <typename TC, int BN, int NT>
+struct CStage {
+  static constexpr int kRowBytes = BN * (int)sizeof(TC);
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kSwz = (kChunks < 32 ? kChunks : 32) - 1;
+  __device__ __forceinline__ static int off(int r, int c) {   // column c (a multiple of 4) of staged row r
+    const int byte = c * (int)sizeof(TC);
+    return r * kRowBytes + (((byte >> 4) ^ (r & kSwz)) << 4) + (byte & 15);
+  }
+  __device__ __forceinline__ static void put4(char* lds, int r, int c, const float* v) {
+    if constexpr (sizeof(TC) == 2) {
+      store4(reinterpret_cast<bf16*>(lds + off(r, c)), v[0], v[1], v[2], v[3]);
+    } else {
+      *reinterpret_cast<f32x4*>(lds + off(r, c)) = f32x4{v[0], v[1], v[2], v[3]};
+    }
+  }
+  // staged rows [0, rows) -> C rows m0.., columns n0..
+  __device__ __forceinline__ static void flush(const char* lds, int rows, char* C, int64_t ldc, int m0, int n0, int M,
+                                               int N, int tid) {
+    for (int idx = tid; idx < rows * kChunks; idx += NT) {
+      const int r = idx / kChunks, ch = idx % kChunks;
+      const int m = m0 + r, n = n0 + ch * (16 / (int)sizeof(TC));
+      if (m < M && n < N) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * kRowBytes + ((ch ^ (r & kSwz)) << 4));
+        *reinterpret_cast<u32x4*>(C + ((int64_t)m * ldc + n) * (int)sizeof(TC)) = v;
+      }
+    }
+  }
+};
+
 template <int BM, int BN, int WGM, int WGN, bool A_K, bool B_K, bool DMA, int EPI, typename TC>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN, TM = WTM / 32, TN = WTN / 32;
-  constexpr int kStage = (BM + BN) * 128;
+  constexpr int kBOff = tile_bytes<BM, DMA>();                 // B tile offset in a stage
+  constexpr int kStage = kBOff + tile_bytes<BN, DMA>();
   __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
 
   const int lane = threadIdx.x & 63;
@@ -532,18 +585,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
   TPL_ISSUE_TILES(0, smem);
   if constexpr (!DMA) {
     tA.store(smem);
-    tB.store(smem + BM * 128);
+    tB.store(smem + kBOff);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
-  read_frags<BM, BN, A_K, B_K, TM, TN>(fa[0], fb[0], smem, 0, wm * WTM, wn * WTN, lane);
+  read_frags<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], smem, 0, wm * WTM, wn * WTN, lane);
 
   for (int kt = 0; kt < KT; ++kt) {
     const char* cur = smem + (kt & 1) * kStage;
     char* nxt = smem + ((kt + 1) & 1) * kStage;
     // step 0: fragments of step 1 (first, so no LDS write is ordered before
     // them), then the loads of the next tile, around this step's MFMAs
-    read_frags<BM, BN, A_K, B_K, TM, TN>(fa[1], fb[1], cur, 1, wm * WTM, wn * WTN, lane);
+    read_frags<BM, BN, A_K, B_K, DMA, TM, TN>(fa[1], fb[1], cur, 1, wm * WTM, wn * WTN, lane);
     TPL_ISSUE_TILES(kt + 1, nxt);
     mfma_tile<TM, TN>(acc, fa[0], fb[0]);
 #pragma unroll
@@ -553,17 +606,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
       if (x < kVm) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
     }
     // steps 1, 2
-    read_frags<BM, BN, A_K, B_K, TM, TN>(fa[0], fb[0], cur, 2, wm * WTM, wn * WTN, lane);
+    read_frags<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], cur, 2, wm * WTM, wn * WTN, lane);
     mfma_tile<TM, TN>(acc, fa[1], fb[1]);
 #pragma unroll
     for (int x = 0; x < kMf; ++x) {
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
       if (x < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
     }
-    read_frags<BM, BN, A_K, B_K, TM, TN>(fa[1], fb[1], cur, 3, wm * WTM, wn * WTN, lane);
+    read_frags<BM, BN, A_K, B_K, DMA, TM, TN>(fa[1], fb[1], cur, 3, wm * WTM, wn * WTN, lane);
     if constexpr (!DMA) {   // stage `nxt` is free since the last barrier
       tA.store(nxt);
-      tB.store(nxt + BM * 128);
+      tB.store(nxt + kBOff);
     }
     mfma_tile<TM, TN>(acc, fa[0], fb[0]);
 #pragma unroll
@@ -579,7 +632,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
     for (int x = 0; x < kHead; ++x) mfma_step(acc[x / TN][x % TN], fb[1][x % TN], fa[1][x / TN]);
     __builtin_amdgcn_s_waitcnt(0);          // this wave's loads of tile kt+1 have landed, its reads are done
     __builtin_amdgcn_s_barrier();            // ... and every other wave's
-    read_frags<BM, BN, A_K, B_K, TM, TN>(fa[0], fb[0], nxt, 0, wm * WTM, wn * WTN, lane);
+    read_frags<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], nxt, 0, wm * WTM, wn * WTN, lane);
 #pragma unroll
     for (int x = kHead; x < kMf; ++x) mfma_step(acc[x / TN][x % TN], fb[1][x % TN], fa[1][x / TN]);
 #pragma unroll
@@ -594,7 +647,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
     const char* cur = smem + (KT & 1) * kStage;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      if (st > 0) read_frags<BM, BN, A_K, B_K, TM, TN>(fa[0], fb[0], cur, st, wm * WTM, wn * WTN, lane);
+      if (st > 0) read_frags<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], cur, st, wm * WTM, wn * WTN, lane);
       if (KT * 64 + 16 * st + 8 * (lane >> 5) >= g.K) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) zero_frag(fa[0][i]);
@@ -606,35 +659,61 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
   }
   (void)kt_all;
 
+  // epilogue through LDS (the stages are free once every wave is past its
+  // last fragment read); fp32 tiles that exceed the LDS go in row passes
+  using Stage = CStage<TC, BN, NW * 64>;
+  constexpr int kCap = 2 * kStage / Stage::kRowBytes;   // rows the LDS holds
+  constexpr int kRP = kCap >= BM ? BM : (kCap >= 128 ? 128 : (kCap >= 64 ? 64 : 32));
+  static_assert(kRP >= WTM && BM % kRP == 0 && kRP % WTM == 0, "staging rows must hold whole wave tiles");
+  constexpr int kRounds = EPI == EPI_BIAS_GELU ? 2 : 1;   // u, then GeLU(u)
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * WTM + i * 32 + (lane & 31);
-    if (m >= g.M) continue;
+  for (int round = 0; round < kRounds; ++round) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int p = 0; p < BM / kRP; ++p) {
+      if ((wm * WTM) / kRP == p) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
-        if (n >= g.N) continue;
-        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
-          float b[4];
-          load4(reinterpret_cast<const bf16*>(g.bias) + n, b);
+        for (int i = 0; i < TM; ++i) {
+          const int rt = wm * WTM + i * 32 + (lane & 31);   // row within the tile
+          const int m = m0 + rt;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += b[e];
-        }
-        if constexpr (EPI == EPI_DGELU) {
-          float u[4];
-          load4(reinterpret_cast<const bf16*>(g.C2) + (int64_t)m * g.ldc2 + n, u);
+          for (int j = 0; j < TN; ++j) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
-        }
-        store4(reinterpret_cast<TC*>(g.C) + (int64_t)m * g.ldc + n, v[0], v[1], v[2], v[3]);
-        if constexpr (EPI == EPI_BIAS_GELU) {
-          bf16* ap = reinterpret_cast<bf16*>(g.C2) + (int64_t)m * g.ldc2 + n;
-          store4(ap, gelu_f(v[0]), gelu_f(v[1]), gelu_f(v[2]), gelu_f(v[3]));
+            for (int q = 0; q < 4; ++q) {
+              const int nt = wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+              const int n = n0 + nt;
+              float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
+                if (n < g.N) {
+                  float b[4];
+                  load4(reinterpret_cast<const bf16*>(g.bias) + n, b);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) v[e] += b[e];
+                }
+              }
+              if constexpr (EPI == EPI_DGELU) {
+                if (m < g.M && n < g.N) {
+                  float u[4];
+                  load4(reinterpret_cast<const bf16*>(g.C2) + (int64_t)m * g.ldc2 + n, u);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
+                }
+              }
+              if constexpr (EPI == EPI_BIAS_GELU) {
+                if (round == 1) {
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
+                }
+              }
+              Stage::put4(smem, rt - p * kRP, nt, v);
+            }
+          }
         }
       }
+      __syncthreads();
+      Stage::flush(smem, kRP, round == 0 ? g.C : g.C2, round == 0 ? g.ldc : g.ldc2, m0 + p * kRP, n0, g.M, g.N,
+                   (int)threadIdx.x);
+      __syncthreads();
     }
   }
 }
