@@ -772,13 +772,12 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // rb + 32i + lane%32, columns nb + ...): rounds to bf16 once, stores the
 // packed values, and writes per row (max, sum exp(l - max)) over the wave's
 // columns to xs[row within the tile]. FULL: every column is below N.
-template <int TM, int TN, bool FULL, int BM>
-__device__ __forceinline__ void xent_tile_stats(const Args& g, f32x16 (&acc)[TM][TN], float (&xs)[BM][2], int m0,
-                                                int nb, int rb, int lane) {
+template <int TM, int TN, bool FULL, int BM, int BN>
+__device__ __forceinline__ void xent_tile_stats(const Args& g, f32x16 (&acc)[TM][TN], float (&xs)[BM][2], char* stg,
+                                                int n0, int nb, int rb, int lane) {
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int rt = rb + i * 32 + (lane & 31);
-    const int m = m0 + rt;
     uint32_t pk[TN][8];
     float mx = -INFINITY;
 #pragma unroll
@@ -824,18 +823,14 @@ __device__ __forceinline__ void xent_tile_stats(const Args& g, f32x16 (&acc)[TM]
       xs[rt][0] = mx;
       xs[rt][1] = se;
     }
-    if (m < g.M) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = nb + j * 32 + 8 * q + 4 * (lane >> 5);
-          if (FULL || n < g.N) {
-            u32x2 v = {pk[j][2 * q], pk[j][2 * q + 1]};
-            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16*>(g.C) + (int64_t)m * g.ldc + n) = v;
-          }
-        }
-    }
+      for (int q = 0; q < 4; ++q) {
+        const int nt = nb - n0 + j * 32 + 8 * q + 4 * (lane >> 5);   // column within the tile
+        u32x2 v = {pk[j][2 * q], pk[j][2 * q + 1]};
+        *reinterpret_cast<u32x2*>(stg + CStage<bf16, BN, 64>::off(rt, nt)) = v;
+      }
   }
 }
 
@@ -964,11 +959,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
     // of a row in a wave; the WGN waves of a row are merged through LDS in
     // wave order. (The target logit is read back by the merge kernel.)
     __shared__ float xs[WGN][BM][2];
+    static_assert(NS * kStage >= BM * BN * 2, "the stages must hold the staged bf16 tile");
+    __syncthreads();   // every wave is past its last fragment read: the stages are free
     if (n0 + BN <= g.N)
-      xent_tile_stats<TM, TN, true>(g, acc, xs[wn], m0, n0 + wn * WTN, wm * WTM, lane);
+      xent_tile_stats<TM, TN, true, BM, BN>(g, acc, xs[wn], smem, n0, n0 + wn * WTN, wm * WTM, lane);
     else
-      xent_tile_stats<TM, TN, false>(g, acc, xs[wn], m0, n0 + wn * WTN, wm * WTM, lane);
+      xent_tile_stats<TM, TN, false, BM, BN>(g, acc, xs[wn], smem, n0, n0 + wn * WTN, wm * WTM, lane);
     __syncthreads();
+    CStage<bf16, BN, NW * 64>::flush(smem, BM, g.C, g.ldc, m0, n0, g.M, g.N, (int)threadIdx.x);
     for (int rt = threadIdx.x; rt < BM; rt += NW * 64) {
       const int m = m0 + rt;
       if (m >= g.M) continue;
@@ -989,30 +987,46 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
     return;
   }
 
+  // epilogue through LDS (all four stages, once every wave is past its last
+  // fragment read)
+  using Stage = CStage<TC, BN, NW * 64>;
+  static_assert(NS * kStage >= BM * Stage::kRowBytes, "the stages must hold the staged tile");
+  constexpr int kRounds = EPI == EPI_BIAS_GELU ? 2 : 1;   // u, then GeLU(u)
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * WTM + i * 32 + (lane & 31);
-    if (m >= g.M) continue;
+  for (int round = 0; round < kRounds; ++round) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int i = 0; i < TM; ++i) {
+      const int rt = wm * WTM + i * 32 + (lane & 31);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
-        if (n >= g.N) continue;
-        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
-          float b[4];
-          load4(reinterpret_cast<const bf16*>(g.bias) + n, b);
+      for (int j = 0; j < TN; ++j) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += b[e];
-        }
-        store4(reinterpret_cast<TC*>(g.C) + (int64_t)m * g.ldc + n, v[0], v[1], v[2], v[3]);
-        if constexpr (EPI == EPI_BIAS_GELU) {
-          bf16* ap = reinterpret_cast<bf16*>(g.C2) + (int64_t)m * g.ldc2 + n;
-          store4(ap, gelu_f(v[0]), gelu_f(v[1]), gelu_f(v[2]), gelu_f(v[3]));
+        for (int q = 0; q < 4; ++q) {
+          const int nt = wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
+          const int n = n0 + nt;
+          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
+            if (n < g.N) {
+              float b[4];
+              load4(reinterpret_cast<const bf16*>(g.bias) + n, b);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] += b[e];
+            }
+          }
+          if constexpr (EPI == EPI_BIAS_GELU) {
+            if (round == 1) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
+            }
+          }
+          Stage::put4(smem, rt, nt, v);
         }
       }
     }
+    __syncthreads();
+    Stage::flush(smem, BM, round == 0 ? g.C : g.C2, round == 0 ? g.ldc : g.ldc2, m0, n0, g.M, g.N,
+                 (int)threadIdx.x);
+    __syncthreads();
   }
 }
 
