@@ -85,6 +85,8 @@ def traced_kernels(st, steps, B, dtype):
 
 
 def roofline(agg, dtype):
+    if not agg:   # no traced steps (--trace-steps 0)
+        return None
     name, (count, ms, work) = max(agg.items(), key=lambda kv: kv[1][1])
     traffic = measured_traffic(name)
     if name in MFMA_KERNELS:
