@@ -27,6 +27,7 @@ __all__ = [
     "attn_block_fwd", "attn_block_bwd_shard", "mlp_block_fwd", "mlp_block_bwd_shard",
     "block_bwd_replicated", "partial_sum", "layer_fwd", "layer_bwd",
     "xent_logits", "xent_local_stats", "xent_finish", "xent_full", "xent_bwd_local",
+    "embedding_fwd_shard", "embedding_bwd_shard",
     "layer_flops",
 ]
 
@@ -311,6 +312,36 @@ def xent_bwd_local(logits, lse, targets, v0, mask, dloss, hidden, emb):
     dl[inside, t[inside]] -= 1.0
     dl *= g[:, None]
     return dl, dl @ _f(emb), dl.T @ _f(hidden)
+
+
+# ---------------------------------------------------------------------------
+# vocabulary-parallel input embedding (guide page section 3.3: the input
+# layer is split along the vocabulary and the ranks' outputs are summed by an
+# all-reduce)
+
+def embedding_fwd_shard(tokens, emb_in, v0):
+    """This rank's partial of the input embedding: row n is E_in[tok_n - v0]
+    when the id lies in the rank's range [v0, v0 + V_r), else zero. The sum of
+    the ranks' partials (the all-reduce) is the full lookup E_in[tok_n]."""
+    emb_in = _f(emb_in)
+    vr = emb_in.shape[0]
+    t = np.asarray(tokens, np.int64) - v0
+    out = np.zeros((len(t), emb_in.shape[1]))
+    inside = np.nonzero((t >= 0) & (t < vr))[0]
+    out[inside] = emb_in[t[inside]]
+    return out
+
+
+def embedding_bwd_shard(tokens, d_out, v0, vr):
+    """Gradient of this rank's rows of E_in given the (replicated) gradient of
+    the summed embedding output: d_E[v] = sum of d_out[n] over the rows n whose
+    id is v0 + v (a scatter-add; ids outside the range contribute nothing)."""
+    d_out = _f(d_out)
+    t = np.asarray(tokens, np.int64) - v0
+    grad = np.zeros((vr, d_out.shape[1]))
+    inside = np.nonzero((t >= 0) & (t < vr))[0]
+    np.add.at(grad, t[inside], d_out[inside])
+    return grad
 
 
 # ---------------------------------------------------------------------------

@@ -134,6 +134,7 @@ _TENSOR_IDS = {
     "ln2_b": 8, "b_o": 9, "b_2": 10, "wq": 11, "wk": 12, "wv": 13, "bq": 14, "bk": 15,
     "bv": 16, "wo": 17, "w1": 18, "b1": 19, "w2": 20, "emb": 21, "h1": 22,
     "dsum_attn": 23, "dsum_mlp": 24, "peer_stats": 25, "peer_partials": 26,
+    "tokens": 27, "emb_in": 28, "dx_emb": 29,
 }
 
 
@@ -300,3 +301,23 @@ def device_shard(cfg: Config, s: RankShard) -> dict:
 def storage(cfg: Config, a: np.ndarray) -> np.ndarray:
     """Host array in the storage dtype (uint16 bits for bf16, float32 otherwise)."""
     return bf16_bits(a) if cfg.dtype == "bf16" else np.ascontiguousarray(a, np.float32)
+
+
+# ---------------------------------------------------------------------------
+# vocabulary-parallel input embedding (guide page section 3.3)
+
+def input_tokens(cfg: Config, skew: int = 0) -> np.ndarray:
+    """[N] int32 input ids, uniform in [0, V); with skew > 0 drawn from the
+    first `skew` ids only (many repeated ids, for the gradient's scatter-add)."""
+    hi = cfg.vocab if skew <= 0 else min(skew, cfg.vocab)
+    return _rng(cfg, "tokens").integers(0, hi, size=cfg.rows, dtype=np.int64).astype(np.int32)
+
+
+def input_emb_shard(cfg: Config, r: int) -> np.ndarray:
+    """E_in rows [r*V_r, (r+1)*V_r) of the input embedding, [V_r, h], N(0, sigma_w)."""
+    return _normal(cfg, "emb_in", (cfg.vocab_r, cfg.hidden), cfg.sigma_w, rank=r)
+
+
+def embedding_grad_in(cfg: Config) -> np.ndarray:
+    """Upstream gradient of the embedding output, [N, h], N(0, 1)."""
+    return _normal(cfg, "dx_emb", (cfg.rows, cfg.hidden))

@@ -390,3 +390,56 @@ def test_flop_count_counts_visible_pairs():
                + 2 * n * cfg.hidden_r * h + 4 * n * h * cfg.ffn_r)
         assert f["layer"] == 3 * fwd
     assert round(O.layer_flops(synth.get_config("gpt2_355m_t1"))["layer"] / 1e9, 1) == 670.1
+
+
+# ---------------------------------------------------------------------------
+# vocabulary-parallel input embedding (guide page section 3.3)
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_embedding_partials_sum_to_the_lookup(t):
+    """Each rank looks up only its vocabulary rows; the all-reduce of the
+    partials is torch's embedding lookup over the whole table, exactly."""
+    g = np.random.default_rng(7)
+    V, h, n = 64, 24, 200
+    E = g.standard_normal((V, h))
+    tok = g.integers(0, V, size=n)
+    tok[:10] = tok[10]                      # repeated ids
+    ref = F.embedding(torch.from_numpy(tok), torch.from_numpy(E)).numpy()
+    vr = V // t
+    parts = [O.embedding_fwd_shard(tok, E[r * vr:(r + 1) * vr], r * vr) for r in range(t)]
+    np.testing.assert_array_equal(sum(parts), ref)
+    # a row is non-zero on exactly the rank that owns its id
+    owner = tok // vr
+    for r, p in enumerate(parts):
+        assert np.all(np.any(p != 0, axis=1) == (owner == r))
+
+
+@pytest.mark.parametrize("t", [1, 4])
+def test_embedding_bwd_matches_autograd(t):
+    g = np.random.default_rng(8)
+    V, h, n = 48, 16, 300
+    E = torch.from_numpy(g.standard_normal((V, h))).requires_grad_(True)
+    tok = g.integers(0, 12, size=n)          # heavily repeated ids
+    tok[-5:] = g.integers(12, V, size=5)
+    G = g.standard_normal((n, h))
+    (F.embedding(torch.from_numpy(tok), E) * torch.from_numpy(G)).sum().backward()
+    vr = V // t
+    grads = [O.embedding_bwd_shard(tok, G, r * vr, vr) for r in range(t)]
+    np.testing.assert_allclose(np.concatenate(grads), E.grad.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_embedding_bwd_brute_force_and_out_of_range_ids():
+    g = np.random.default_rng(9)
+    vr, h, v0 = 6, 5, 6
+    tok = np.array([6, 7, 6, 11, 0, 12, -1, 6, 9, 100])
+    G = g.standard_normal((len(tok), h))
+    want = np.zeros((vr, h))
+    for i, tid in enumerate(tok):
+        if v0 <= tid < v0 + vr:
+            for c in range(h):
+                want[tid - v0, c] += G[i, c]
+    np.testing.assert_allclose(O.embedding_bwd_shard(tok, G, v0, vr), want, rtol=0, atol=1e-15)
+    E = g.standard_normal((vr, h))
+    out = O.embedding_fwd_shard(tok, E, v0)
+    assert np.all(out[[4, 5, 6, 9]] == 0)     # ids outside [v0, v0+vr) give zero rows
+    np.testing.assert_array_equal(out[0], E[0])
