@@ -153,7 +153,7 @@ def copy_calibration(torch, mib=1024, reps=5):
 # ---------------------------------------------------------------- profile summaries
 
 SOURCES = {"gemm": "gemm.hip", "attn": "attention.hip", "layernorm": "norm.hip", "colsum": "norm.hip",
-           "partial": "norm.hip", "xent": "xent.hip"}
+           "partial": "norm.hip", "xent": "xent.hip", "embedding": "embedding.hip"}
 PROFILE_CMDS = {
     "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_c2 -o c2 -- "
              "python3 <repo>/bench.py --steps 5 --warmup 2 --cpu-seqs 0",
@@ -187,7 +187,9 @@ def kernel_family(name: str) -> str:
              ("attn_fwd", "attn_fwd"), ("ln_bwd_cols", "layernorm_bwd_cols"), ("ln_bwd", "layernorm_bwd"),
              ("ln_fwd", "layernorm_fwd"), ("colsum_final", "colsum_final"), ("colsum", "colsum"),
              ("partial_sum", "partial_sum"), ("xent_stats", "xent_stats"), ("xent_finish", "xent_finish"),
-             ("xent_dlogits", "xent_dlogits"), ("xent_merge", "xent_merge")]
+             ("xent_dlogits", "xent_dlogits"), ("xent_merge", "xent_merge"), ("embed_fwd", "embedding_fwd"),
+             ("embed_grad", "embedding_bwd"), ("embed_keys", "embedding_sort"), ("radix_sort", "embedding_sort"),
+             ("embed_segments", "embedding_sort")]
     for key, fam in table:
         if key in name:
             return fam
@@ -208,6 +210,37 @@ def source_sha(family: str) -> str:
             path = os.path.join(ROOT, "tensor_transformer_layer_03_amd", "csrc", f)
             return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
     return ""
+
+
+def embedding_bench(cfg, steps, torch, B):
+    """The vocabulary-parallel input embedding on this rank's share of the
+    workload (a row beside the layer step, not part of the headline): forward
+    lookup and scatter-add gradient, each timed over `steps` calls."""
+    import synth
+    desc = B.make_desc(cfg.hidden, cfg.heads, cfg.head_dim, cfg.ffn, cfg.tp, 0, cfg.seq, cfg.micro_batch, cfg.vocab,
+                       cfg.causal, cfg.dtype)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    es = 2 if cfg.dtype == "bf16" else 4
+    tok = torch.from_numpy(synth.input_tokens(cfg)).cuda()
+    emb = torch.randn(cfg.vocab_r, cfg.hidden, device="cuda").to(dt)
+    dout = torch.randn(cfg.rows, cfg.hidden, device="cuda").to(dt)
+    part = torch.empty(cfg.rows, cfg.hidden, device="cuda", dtype=dt)
+    grad = torch.empty(cfg.vocab_r, cfg.hidden, device="cuda", dtype=torch.float32)
+    ws = torch.empty(B.vocab_parallel_embedding_ws_bytes(desc), device="cuda", dtype=torch.uint8)
+    fwd = lambda: B.vocab_parallel_embedding_fwd(desc, tok, emb, part)
+    bwd = lambda: B.vocab_parallel_embedding_bwd(desc, tok, dout, grad, ws)
+    for _ in range(3):
+        fwd()
+        bwd()
+    f_ms = time_loop(fwd, steps, torch)
+    b_ms = time_loop(bwd, steps, torch)
+    n, h, vr = cfg.rows, cfg.hidden, cfg.vocab_r
+    f_bytes = 2 * n * h * es + 4 * n                 # rows read (ids in range) + partial written + ids
+    b_bytes = n * h * es + vr * h * 4 + 4 * n        # gradient rows read once + fp32 table written + ids
+    return {"workload": f"{cfg.name}: ids {n}, rank rows V_r {vr} x h {h}, uniform ids",
+            "fwd_us": round(f_ms * 1e3, 2), "fwd_gbs": round(f_bytes / (f_ms / 1e3) / 1e9, 1),
+            "bwd_us": round(b_ms * 1e3, 2), "bwd_gbs": round(b_bytes / (b_ms / 1e3) / 1e9, 1),
+            "bound": "hbm", "peak_gbs": 8000.0}
 
 
 def summarize_profiles(d: str, workload: str):
@@ -327,6 +360,7 @@ def main():
                 if args.layer_only else None)
     agg = traced_kernels(st, args.trace_steps, B, cfg.dtype)
     loss = float(st.shared["loss"][0].item())
+    emb = embedding_bench(cfg, args.steps, torch, B)
 
     value = fl["total"] / (ms / 1e3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
@@ -358,6 +392,7 @@ def main():
             "note": "layer fwd+bwd with its 4 all-reduce stand-ins, loss excluded"},
         "loss": round(loss, 6),
         "roofline": roofline(agg, cfg.dtype),
+        "embedding": emb,
         "kernels_per_step": [{"kernel": k, "launches": c // args.trace_steps, "ms": round(t, 4),
                               ("tflops" if k in MFMA_KERNELS else "gbs"):
                                   round(w / args.trace_steps / (t / 1e3) / (1e12 if k in MFMA_KERNELS else 1e9), 1)}

@@ -189,6 +189,26 @@ tpl_status vocab_parallel_xent_fwd(const tpl_desc* desc, tpl_xent_phase phase,
                                    const float* const* all_stats, float* lse, float* loss_rows,
                                    float* loss, void* stream);
 
+/* Vocabulary-parallel input embedding (guide page 3.3: the input layer is
+ * split along the vocabulary and the ranks' outputs summed by an all-reduce).
+ *   fwd: x_partial [N][h] (storage dtype) row n = E_r[tokens[n] - rank*V_r] if
+ *     the id lies in this rank's range [rank*V_r, (rank+1)*V_r), else zeros.
+ *     shard_partial_sum over the ranks' partials (the all-reduce) gives the
+ *     lookup E[tokens[n]].
+ *   bwd: from d_out [N][h] (storage dtype; the gradient of the summed output,
+ *     the same on every rank), d_emb_in [V_r][h] fp32 (overwritten) row v =
+ *     sum of d_out[n] over the rows whose id is rank*V_r + v, added in
+ *     ascending n (a stable sort of the ids, no float atomics: deterministic);
+ *     rows no id points to are zero. No communication.
+ * tokens: [N] int32 global ids (ids outside [0, V) contribute nothing);
+ * emb_in: E_r [V_r][h] storage dtype; workspace: device scratch of
+ * vocab_parallel_embedding_ws_bytes(desc) bytes, overwritten. */
+size_t vocab_parallel_embedding_ws_bytes(const tpl_desc* desc);
+tpl_status vocab_parallel_embedding_fwd(const tpl_desc* desc, const int32_t* tokens, const void* emb_in,
+                                        void* x_partial, void* stream);
+tpl_status vocab_parallel_embedding_bwd(const tpl_desc* desc, const int32_t* tokens, const void* d_out,
+                                        float* d_emb_in, void* workspace, void* stream);
+
 /* Vocabulary-parallel cross-entropy backward for this rank.
  *   dlogits = g_n (exp(logits - lse_n) - [j == targets[n] - rank*V_r]) with
  *   g_n = dloss * mask[n] / loss[1], written IN PLACE over `logits`;

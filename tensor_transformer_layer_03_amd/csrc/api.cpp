@@ -153,7 +153,7 @@ int g_trace_cap = 0, g_trace_used = 0;
 const char* const kKernelNames[K_COUNT] = {
     "gemm_nt", "gemm_nn", "gemm_tn", "attn_fwd", "attn_bwd_pre", "attn_bwd_dq", "attn_bwd_dkdv",
     "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_cols", "colsum", "colsum_final", "partial_sum",
-    "xent_stats", "xent_finish", "xent_dlogits", "xent_merge"};
+    "xent_stats", "xent_finish", "xent_dlogits", "xent_merge", "embedding_fwd", "embedding_sort", "embedding_bwd"};
 
 }  // namespace
 
@@ -417,6 +417,32 @@ tpl_status vocab_parallel_xent_bwd(const tpl_desc* desc, const void* hidden, con
   GemmDesc ge = gemm(m, false, false, m.vr, m.h, m.N, logits, m.vr, hidden, m.h, d_emb, m.h);
   ge.c_f32 = true;
   return from_hip(launch_gemm(ge, s));
+}
+
+size_t vocab_parallel_embedding_ws_bytes(const tpl_desc* desc) {
+  Dims m;
+  if (check_desc(desc, &m) != TPL_OK) return 0;
+  return round256(embedding_ws_bytes(m.N, (int)m.vr));
+}
+
+tpl_status vocab_parallel_embedding_fwd(const tpl_desc* desc, const int32_t* tokens, const void* emb_in,
+                                        void* x_partial, void* stream) {
+  Dims m;
+  tpl_status st = check_desc(desc, &m);
+  if (st != TPL_OK) return st;
+  if (!ok_ptr(tokens) || !ok_ptr(emb_in) || !ok_ptr(x_partial)) return TPL_ERR_INVALID_ARG;
+  return from_hip(launch_embedding_fwd(m.dt, tokens, emb_in, x_partial, m.N, (int)m.h, (int64_t)desc->rank * m.vr,
+                                       (int)m.vr, static_cast<hipStream_t>(stream)));
+}
+
+tpl_status vocab_parallel_embedding_bwd(const tpl_desc* desc, const int32_t* tokens, const void* d_out,
+                                        float* d_emb_in, void* workspace, void* stream) {
+  Dims m;
+  tpl_status st = check_desc(desc, &m);
+  if (st != TPL_OK) return st;
+  if (!ok_ptr(tokens) || !ok_ptr(d_out) || !ok_ptr(d_emb_in) || !ok_ptr(workspace)) return TPL_ERR_INVALID_ARG;
+  return from_hip(launch_embedding_bwd(m.dt, tokens, d_out, d_emb_in, m.N, (int)m.h, (int64_t)desc->rank * m.vr,
+                                       (int)m.vr, workspace, static_cast<hipStream_t>(stream)));
 }
 
 tpl_status tpl_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajor, int64_t M, int64_t N, int64_t K, const void* A,

@@ -13,7 +13,8 @@ inline size_t dtype_size(int dt) { return dt == DT_BF16 ? 2 : 4; }
 enum KernelId {
   K_GEMM_NT = 0, K_GEMM_NN, K_GEMM_TN, K_ATTN_FWD, K_ATTN_BWD_PRE, K_ATTN_BWD_DQ,
   K_ATTN_BWD_DKDV, K_LN_FWD, K_LN_BWD, K_LN_BWD_COLS, K_COLSUM, K_COLSUM_FINAL,
-  K_PARTIAL_SUM, K_XENT_STATS, K_XENT_FINISH, K_XENT_DLOGITS, K_XENT_MERGE, K_COUNT
+  K_PARTIAL_SUM, K_XENT_STATS, K_XENT_FINISH, K_XENT_DLOGITS, K_XENT_MERGE, K_EMB_FWD, K_EMB_SORT, K_EMB_BWD,
+  K_COUNT
 };
 const char* kernel_name(int id);
 struct TraceScope {
@@ -105,5 +106,13 @@ hipError_t launch_xent_finish(const float* const* all_stats, int t, int64_t rows
 hipError_t launch_xent_dlogits(int dtype, void* logits, int64_t rows, int vr,
                                const int32_t* targets, int64_t v0, const uint8_t* mask,
                                const float* lse, const float* loss, float dloss, hipStream_t s);
+
+// ------------------------------------------------------------------ input embedding
+// Workspace bytes of the backward (sort keys / values twice, segment starts).
+size_t embedding_ws_bytes(int64_t rows, int vr);
+hipError_t launch_embedding_fwd(int dtype, const int32_t* tokens, const void* emb, void* out, int64_t rows, int cols,
+                                int64_t v0, int vr, hipStream_t s);
+hipError_t launch_embedding_bwd(int dtype, const int32_t* tokens, const void* d_out, float* d_emb, int64_t rows,
+                                int cols, int64_t v0, int vr, void* ws, hipStream_t s);
 
 }  // namespace tpl
