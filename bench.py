@@ -212,6 +212,20 @@ def source_sha(family: str) -> str:
     return ""
 
 
+def recompute_bench(st, steps, torch):
+    """Layer backward with the forward stash kept vs rebuilt from the block
+    inputs (activation recomputation): time of each and the per-layer stash
+    the recomputing form no longer has to keep (one buffer serves all layers)."""
+    st.recompute = False
+    bwd_ms = time_loop(st.backward, steps, torch)
+    st.recompute = True
+    rec_ms = time_loop(st.backward, steps, torch)
+    st.recompute = False
+    stash = sum(t.tensors["saved_attn"].numel() + t.tensors["saved_mlp"].numel() for t in st.states)
+    return {"bwd_ms": round(bwd_ms, 4), "bwd_recompute_ms": round(rec_ms, 4),
+            "stash_bytes_per_layer": int(stash)}
+
+
 def embedding_bench(cfg, steps, torch, B):
     """The vocabulary-parallel input embedding on this rank's share of the
     workload (a row beside the layer step, not part of the headline): forward
@@ -361,6 +375,7 @@ def main():
     agg = traced_kernels(st, args.trace_steps, B, cfg.dtype)
     loss = float(st.shared["loss"][0].item())
     emb = embedding_bench(cfg, args.steps, torch, B)
+    rec = recompute_bench(st, max(3, args.steps // 2), torch)
 
     value = fl["total"] / (ms / 1e3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
@@ -393,6 +408,7 @@ def main():
         "loss": round(loss, 6),
         "roofline": roofline(agg, cfg.dtype),
         "embedding": emb,
+        "recompute": rec,
         "kernels_per_step": [{"kernel": k, "launches": c // args.trace_steps, "ms": round(t, 4),
                               ("tflops" if k in MFMA_KERNELS else "gbs"):
                                   round(w / args.trace_steps / (t / 1e3) / (1e12 if k in MFMA_KERNELS else 1e9), 1)}

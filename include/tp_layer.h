@@ -61,7 +61,7 @@ typedef enum {
 
 typedef enum { TPL_F32 = 0, TPL_BF16 = 1 } tpl_dtype;
 typedef enum { TPL_BLOCK_ATTN = 0, TPL_BLOCK_MLP = 1 } tpl_block;
-typedef enum { TPL_BWD_SHARD = 0, TPL_BWD_REPLICATED = 1 } tpl_bwd_phase;
+typedef enum { TPL_BWD_SHARD = 0, TPL_BWD_REPLICATED = 1, TPL_BWD_SHARD_RECOMPUTE = 2 } tpl_bwd_phase;
 typedef enum { TPL_XENT_LOCAL = 0, TPL_XENT_FINISH = 1 } tpl_xent_phase;
 
 /* The problem statement of the pages: hidden size, heads, TP degree and rank,
@@ -151,8 +151,17 @@ tpl_status shard_partial_sum(const tpl_desc* desc, const void* const* partials, 
  *   TPL_BWD_REPLICATED: from dy, d_ln_sum (= sum over ranks of d_ln_partial),
  *     the block input x and `saved`, writes dx = dy + LN_bwd(d_ln_sum) [N][h]
  *     and grads->d_ln_g, d_ln_b, d_b_out.
- * Unused pointers for a phase may be NULL. `saved` must come from
- * tp_layer_shard_fwd with the same desc, block, x and params; its scratch part
+ *   TPL_BWD_SHARD_RECOMPUTE: activation recomputation (overview page section
+ *     3: checkpointing trades compute for memory). As TPL_BWD_SHARD, but the
+ *     block's forward stash (LN output and statistics; ATTN: qkv, ctx, LSE;
+ *     MLP: u and GeLU(u)) is first recomputed from the block input x into
+ *     `saved`, so `saved` need not hold this block's forward: one buffer of
+ *     tp_layer_saved_bytes can serve every layer of a model. Results are
+ *     identical to TPL_BWD_SHARD. A later TPL_BWD_REPLICATED call with the
+ *     same `saved` uses the recomputed LN statistics.
+ * Unused pointers for a phase may be NULL. For TPL_BWD_SHARD and
+ * TPL_BWD_REPLICATED `saved` must come from tp_layer_shard_fwd (or a
+ * recomputing call) with the same desc, block, x and params; its scratch part
  * is overwritten. */
 tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_phase phase,
                               const void* dy, const void* d_ln_sum, const void* x,

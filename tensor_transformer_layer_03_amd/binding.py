@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libtplayer.so")
 TPL_OK, TPL_ERR_INVALID_ARG, TPL_ERR_UNSUPPORTED, TPL_ERR_HIP = 0, 1, 2, 3
 TPL_F32, TPL_BF16 = 0, 1
 TPL_BLOCK_ATTN, TPL_BLOCK_MLP = 0, 1
-TPL_BWD_SHARD, TPL_BWD_REPLICATED = 0, 1
+TPL_BWD_SHARD, TPL_BWD_REPLICATED, TPL_BWD_SHARD_RECOMPUTE = 0, 1, 2
 TPL_XENT_LOCAL, TPL_XENT_FINISH = 0, 1
 
 

@@ -228,17 +228,15 @@ size_t tp_layer_saved_bytes(const tpl_desc* desc, tpl_block block) {
   return saved_layout(m, block).total;
 }
 
-tpl_status tp_layer_shard_fwd(const tpl_desc* desc, tpl_block block, const void* x,
-                              const tpl_block_params* p, void* partial, void* saved, void* stream) {
-  Dims m;
-  tpl_status st = check_desc(desc, &m);
-  if (st != TPL_OK) return st;
-  if (block != TPL_BLOCK_ATTN && block != TPL_BLOCK_MLP) return TPL_ERR_INVALID_ARG;
-  if (!p || !ok_ptr(x) || !ok_ptr(partial) || !ok_ptr(saved) || !ok_ptr(p->ln_g) || !ok_ptr(p->ln_b) ||
-      !ok_ptr(p->w_in) || !ok_ptr(p->b_in) || !ok_ptr(p->w_out))
-    return TPL_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Saved L = saved_layout(m, block);
+}  // extern "C"
+
+namespace {
+// The block's forward up to (not including) the row-parallel product: LN into
+// `saved`, then ATTN: qkv = y W_qkv^T + b, attention -> ctx, LSE; MLP: u = z
+// W_1^T + b, act = GeLU(u). Used by the forward and by the recomputing
+// backward.
+tpl_status fwd_stash(const Dims& m, const tpl_desc* desc, tpl_block block, const void* x, const tpl_block_params* p,
+                     void* saved, const Saved& L, hipStream_t s) {
   float* mu = slot<float>(saved, L, S_MU);
   float* rstd = slot<float>(saved, L, S_RSTD);
   void* y = slot<char>(saved, L, S_Y);
@@ -256,7 +254,6 @@ tpl_status tp_layer_shard_fwd(const tpl_desc* desc, tpl_block block, const void*
     a.qkv = qkv; a.ld_qkv = 3 * m.hr; a.ctx = ctx; a.ld_ctx = m.hr;
     a.lse = slot<float>(saved, L, S_LSE);
     TPL_TRY(launch_attn_fwd(a, s));
-    TPL_TRY(launch_gemm(gemm(m, true, true, m.N, m.h, m.hr, ctx, m.hr, p->w_out, m.hr, partial, m.h), s));
   } else {
     void* u = slot<char>(saved, L, S_U);
     void* act = slot<char>(saved, L, S_ACT);
@@ -266,6 +263,31 @@ tpl_status tp_layer_shard_fwd(const tpl_desc* desc, tpl_block block, const void*
     g.C2 = act;
     g.ldc2 = m.fr;
     TPL_TRY(launch_gemm(g, s));
+  }
+  return TPL_OK;
+}
+}  // namespace
+
+extern "C" {
+
+tpl_status tp_layer_shard_fwd(const tpl_desc* desc, tpl_block block, const void* x,
+                              const tpl_block_params* p, void* partial, void* saved, void* stream) {
+  Dims m;
+  tpl_status st = check_desc(desc, &m);
+  if (st != TPL_OK) return st;
+  if (block != TPL_BLOCK_ATTN && block != TPL_BLOCK_MLP) return TPL_ERR_INVALID_ARG;
+  if (!p || !ok_ptr(x) || !ok_ptr(partial) || !ok_ptr(saved) || !ok_ptr(p->ln_g) || !ok_ptr(p->ln_b) ||
+      !ok_ptr(p->w_in) || !ok_ptr(p->b_in) || !ok_ptr(p->w_out))
+    return TPL_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Saved L = saved_layout(m, block);
+  st = fwd_stash(m, desc, block, x, p, saved, L, s);
+  if (st != TPL_OK) return st;
+  if (block == TPL_BLOCK_ATTN) {
+    void* ctx = slot<char>(saved, L, S_CTX);
+    TPL_TRY(launch_gemm(gemm(m, true, true, m.N, m.h, m.hr, ctx, m.hr, p->w_out, m.hr, partial, m.h), s));
+  } else {
+    void* act = slot<char>(saved, L, S_ACT);
     TPL_TRY(launch_gemm(gemm(m, true, true, m.N, m.h, m.fr, act, m.fr, p->w_out, m.fr, partial, m.h), s));
   }
   return TPL_OK;
@@ -292,11 +314,21 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
   tpl_status st = check_desc(desc, &m);
   if (st != TPL_OK) return st;
   if (block != TPL_BLOCK_ATTN && block != TPL_BLOCK_MLP) return TPL_ERR_INVALID_ARG;
-  if (phase != TPL_BWD_SHARD && phase != TPL_BWD_REPLICATED) return TPL_ERR_INVALID_ARG;
+  if (phase != TPL_BWD_SHARD && phase != TPL_BWD_REPLICATED && phase != TPL_BWD_SHARD_RECOMPUTE)
+    return TPL_ERR_INVALID_ARG;
   if (!p || !gr || !ok_ptr(dy) || !ok_ptr(saved)) return TPL_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Saved L = saved_layout(m, block);
   float* ws = slot<float>(saved, L, S_WS);
+  if (phase == TPL_BWD_SHARD_RECOMPUTE) {
+    // activation recomputation: rebuild the forward stash from the block
+    // input, then the shard backward as usual
+    if (!ok_ptr(x) || !ok_ptr(p->ln_g) || !ok_ptr(p->ln_b) || !ok_ptr(p->b_in) || !ok_ptr(p->w_in))
+      return TPL_ERR_INVALID_ARG;
+    st = fwd_stash(m, desc, block, x, p, saved, L, s);
+    if (st != TPL_OK) return st;
+    phase = TPL_BWD_SHARD;
+  }
   if (phase == TPL_BWD_REPLICATED) {
     if (!ok_ptr(d_ln_sum) || !ok_ptr(x) || !ok_ptr(dx) || !ok_ptr(p->ln_g) || !ok_ptr(gr->d_ln_g) ||
         !ok_ptr(gr->d_ln_b) || !ok_ptr(gr->d_b_out))

@@ -67,8 +67,9 @@ class LayerStep:
     statistics.
     """
 
-    def __init__(self, cfg, rep, shards: dict, peers=(), peer_stats=(), device="cuda"):
+    def __init__(self, cfg, rep, shards: dict, peers=(), peer_stats=(), device="cuda", recompute=False):
         self.cfg = cfg
+        self.recompute = recompute   # backward rebuilds each block's forward stash from its input
         self.device = torch.device(device)
         dt = cfg.dtype
         self.tdtype = torch.bfloat16 if dt == "bf16" else torch.float32
@@ -169,11 +170,19 @@ class LayerStep:
                                       st.tensors["d_emb"], stream)
         self._sum("dH", None, sh["R"], sh["dout"], stream)
 
+    def poison_saved(self):
+        """Overwrite every forward stash (as another layer reusing the buffer
+        would); only a recomputing backward can still be right."""
+        for st in self.states:
+            st.tensors["saved_attn"].fill_(0xFF)
+            st.tensors["saved_mlp"].fill_(0xFF)
+
     def backward(self, stream=None):
         sh = self.shared
+        shard = B.TPL_BWD_SHARD_RECOMPUTE if self.recompute else B.TPL_BWD_SHARD
         for st in self.states:
             t = st.tensors
-            B.tp_layer_shard_bwd(st.desc, B.TPL_BLOCK_MLP, B.TPL_BWD_SHARD, sh["dout"], None, None, st.mlp,
+            B.tp_layer_shard_bwd(st.desc, B.TPL_BLOCK_MLP, shard, sh["dout"], None, sh["h1"], st.mlp,
                                  t["saved_mlp"], t["dln_mlp"], None,
                                  B.block_grads(t["d_w_1"], t["d_b_1"], t["d_w_2"]), stream)
         self._sum("dln_mlp", None, None, sh["dz_sum"], stream)
@@ -183,7 +192,7 @@ class LayerStep:
                              B.block_grads(d_ln_g=sh["d_ln2_g"], d_ln_b=sh["d_ln2_b"], d_b_out=sh["d_b_2"]), stream)
         for st in self.states:
             t = st.tensors
-            B.tp_layer_shard_bwd(st.desc, B.TPL_BLOCK_ATTN, B.TPL_BWD_SHARD, sh["dh1"], None, None, st.attn,
+            B.tp_layer_shard_bwd(st.desc, B.TPL_BLOCK_ATTN, shard, sh["dh1"], None, sh["x"], st.attn,
                                  t["saved_attn"], t["dln_attn"], None,
                                  B.block_grads(t["d_w_qkv"], t["d_b_qkv"], t["d_w_o"]), stream)
         self._sum("dln_attn", None, None, sh["dy_sum"], stream)

@@ -68,3 +68,26 @@ def test_bitwise_repeatable():
     b, _ = run_gpu(small, rep, shards, peers, pstats)
     for k in a:
         assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+@pytest.mark.parametrize("cfg", [SMALL[0], SMALL[1], synth.CONFIGS["gpt2_355m_t1"]], ids=lambda c: c.name)
+def test_recompute_backward_matches_stash(cfg):
+    """Activation recomputation: with every forward stash overwritten after
+    the forward, the recomputing backward gives bitwise the stash-based
+    results."""
+    import torch
+    from tensor_transformer_layer_03_amd.step import LayerStep
+    rep, shards, peers, peer_stats = build_case(cfg)
+    dev = {r: synth.device_shard(cfg, s) for r, s in shards.items()}
+    a = LayerStep(cfg, rep, dev, peers, peer_stats)
+    a.step()
+    b = LayerStep(cfg, rep, dev, peers, peer_stats, recompute=True)
+    b.forward()
+    b.xent_forward()
+    b.xent_backward()
+    b.poison_saved()
+    b.backward()
+    torch.cuda.synchronize()
+    ra, rb = a.results(), b.results()
+    for k in ra:
+        assert np.array_equal(ra[k], rb[k], equal_nan=True), k
