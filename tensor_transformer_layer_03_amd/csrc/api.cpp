@@ -445,7 +445,11 @@ tpl_status vocab_parallel_xent_bwd(const tpl_desc* desc, const void* hidden, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   TPL_TRY(launch_xent_dlogits(m.dt, logits, m.N, m.vr, targets, (int64_t)desc->rank * m.vr, loss_mask, lse, loss,
                               dloss, s));
-  TPL_TRY(launch_gemm(gemm(m, true, false, m.N, m.h, m.vr, logits, m.vr, emb, m.h, d_hidden_partial, m.h), s));
+  // dH first: it may use d_emb (written by dE right after) as split-K scratch
+  GemmDesc gh = gemm(m, true, false, m.N, m.h, m.vr, logits, m.vr, emb, m.h, d_hidden_partial, m.h);
+  gh.ws = d_emb;
+  gh.ws_floats = (size_t)m.vr * m.h;
+  TPL_TRY(launch_gemm(gh, s));
   GemmDesc ge = gemm(m, false, false, m.vr, m.h, m.N, logits, m.vr, hidden, m.h, d_emb, m.h);
   ge.c_f32 = true;
   return from_hip(launch_gemm(ge, s));

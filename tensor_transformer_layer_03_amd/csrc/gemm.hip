@@ -1047,10 +1047,44 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(float* C, int64_t ldc, 
   *reinterpret_cast<f32x4*>(c) = acc;
 }
 
+struct SplitK { int splits, kchunk; };
+
+// C[m][n] (bf16) = ws[0][m][n] + ws[1][m][n] + ... in split order.
+__global__ __launch_bounds__(256) void splitk_sum_bf16_kernel(bf16* C, int64_t ldc, const float* __restrict__ ws,
+                                                              int nsplit, int M, int N) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (int64_t)M * N) return;
+  const int64_t m = i / N, n = i % N;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(ws + i);
+  for (int sp = 1; sp < nsplit; ++sp) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(ws + (int64_t)sp * M * N + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += v[e];
+  }
+  store4(C + m * ldc + n, acc[0], acc[1], acc[2], acc[3]);
+}
+
+// Split of a bf16 data-gradient product (A K-major, B MN-major) whose
+// 256x256 grid is small and whose K is long (the loss's dH over the
+// vocabulary): every split writes fp32 partials into the workspace, summed
+// and rounded once afterwards. Bounded by the workspace capacity.
+SplitK splitk_dgrad_for(int dtype, int64_t M, int64_t N, int64_t K, size_t ws_floats) {
+  SplitK r{1, (int)K};
+  if (dtype != DT_BF16 || getenv("TPL_GEMM_TILE") || M * N <= 0) return r;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles >= 384 || K < 8192) return r;
+  int64_t sp = std::min<int64_t>((512 + tiles - 1) / tiles, K / 4096);
+  sp = std::min<int64_t>(sp, (int64_t)(ws_floats / (size_t)(M * N)));
+  if (sp < 2) return r;
+  const int64_t chunk = ((K + sp - 1) / sp + 63) / 64 * 64;
+  r.splits = (int)((K + chunk - 1) / chunk);
+  r.kchunk = (int)chunk;
+  return r;
+}
+
 // Split of a weight-gradient product (both operands MN-major, fp32 output)
 // that takes the 128x128 tile: enough splits to put about two workgroups on
 // every CU, each split at least 1024 deep in K.
-struct SplitK { int splits, kchunk; };
 SplitK splitk_for(int dtype, int64_t M, int64_t N, int64_t K) {
   SplitK r{1, (int)K};
   if (dtype != DT_BF16 || getenv("TPL_GEMM_TILE")) return r;
@@ -1186,6 +1220,34 @@ hipError_t run_tiles(const GemmDesc& d, hipStream_t s) {
   }
 }
 
+// bf16 dgrad split over K: the 256x256 8-wave kernel writes every split's
+// fp32 partial into the workspace (C = ws, splits s >= 1 at ws + s*M*N), then
+// one pass sums them in split order and rounds to bf16.
+hipError_t run_dgrad_split(const GemmDesc& d, const SplitK& sk, hipStream_t s) {
+  Args a;
+  a.A = static_cast<const char*>(d.A); a.lda = d.lda;
+  a.B = static_cast<const char*>(d.B); a.ldb = d.ldb;
+  a.C = reinterpret_cast<char*>(d.ws); a.ldc = d.N;
+  a.C2 = nullptr; a.ldc2 = 0;
+  a.bias = nullptr;
+  a.M = (int)d.M; a.N = (int)d.N; a.K = (int)d.K;
+  a.tiles_m = (a.M + 255) / 256;
+  a.tiles_n = (a.N + 255) / 256;
+  a.targets = nullptr; a.v0 = 0; a.xpart = nullptr;
+  a.splits = sk.splits;
+  a.kchunk = sk.kchunk;
+  a.ws = d.ws + (int64_t)d.M * d.N;
+  const int nblk = a.tiles_m * a.tiles_n;
+  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, true, false, false, EPI_NONE, float>), dim3(nblk * a.splits),
+                     dim3(512), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t quads = (d.M * d.N + 3) / 4;
+  hipLaunchKernelGGL(splitk_sum_bf16_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
+                     static_cast<bf16*>(d.C), d.ldc, static_cast<const float*>(d.ws), a.splits, a.M, a.N);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
   if (d.a_kmajor && d.b_kmajor) {
@@ -1206,6 +1268,12 @@ hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
   }
   if (d.a_kmajor && !d.b_kmajor) {
     if (d.c_f32) return hipErrorInvalidValue;
+    if constexpr (sizeof(T) == 2) {
+      if (d.epi == EPI_NONE && d.ws) {
+        const SplitK sk = splitk_dgrad_for(d.dtype, d.M, d.N, d.K, d.ws_floats);
+        if (sk.splits > 1) return run_dgrad_split(d, sk, s);
+      }
+    }
     switch (d.epi) {
       case EPI_NONE: return run_tiles<T, true, false, EPI_NONE, T>(d, s);
       case EPI_DGELU: return run_tiles<T, true, false, EPI_DGELU, T>(d, s);

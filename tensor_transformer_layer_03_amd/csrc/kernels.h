@@ -45,8 +45,11 @@ struct GemmDesc {
   void* C; int64_t ldc;
   void* C2; int64_t ldc2;
   const void* bias;
-  // split-K workspace for fp32 outputs (or NULL: never split); see gemm_ws_floats
+  // split-K workspace (or NULL: never split) and its capacity in floats; fp32
+  // weight gradients need gemm_ws_floats, a bf16 dgrad with few tiles and a
+  // long K uses whatever capacity is given (all splits as fp32 partials)
   float* ws;
+  size_t ws_floats;
   // EPI_XENT only: targets [M] (global ids), v0 = first vocabulary id of the
   // columns, xpart = per-tile (max, sum exp) [tile column][M][2]
   const int32_t* targets; int64_t v0; float* xpart;
