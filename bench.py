@@ -177,6 +177,8 @@ def kernel_family(name: str) -> str:
         return "gemm_nt" if ak and bk else ("gemm_nn" if ak else "gemm_tn")
     if "splitk_sum" in name:          # the split-K sum is part of the weight-gradient product's launch
         return "gemm_tn"
+    if "splitk_reduce" in name:       # split-order sum of a split product: fp32 out = wgrad, bf16 out = dgrad
+        return "gemm_tn" if ("IfE" in name or "<float>" in name) else "gemm_nn"
     if "colpart" in name:             # LN-gradient (3 outputs) or bias-gradient (1 output) column partials
         if "Li3E" in name or ", 3>" in name:
             return "layernorm_bwd_cols"
@@ -197,10 +199,11 @@ def kernel_family(name: str) -> str:
 
 
 def attached(name: str) -> bool:
-    """Dispatches that belong to the preceding launch of their family (the
-    split-K sum of a weight-gradient product): their time and bytes count,
-    their dispatch does not count as a launch."""
-    return "splitk_sum" in name
+    """Dispatches that belong to a launch of their family counted once (the
+    split-K sums, and the K-split tail pass that precedes a weight-gradient
+    product's whole rounds): their time and bytes count, their dispatch does
+    not count as a launch."""
+    return "splitk_sum" in name or "splitk_reduce" in name or "tail_kernel" in name
 
 
 def source_sha(family: str) -> str:

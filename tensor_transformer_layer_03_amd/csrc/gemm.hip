@@ -26,6 +26,7 @@
 // dispatcher deals workgroups to the 8 XCDs round-robin, each with its own
 // L2), then walked in groups of kGroupM tile-rows for L2 reuse of B.
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 
@@ -57,6 +58,7 @@ struct Args {
   float* xpart;
   float* ws;       // split-K partials [splits-1][M][N] (split 0 writes C)
   int splits, kchunk;
+  int64_t a_trim;  // bytes of an MN-major A past its last row's M columns that are not the caller's
 };
 
 // Load a K-major operand tile (ROWS x BK) to registers: ROWS*8 chunks of 16 B.
@@ -400,7 +402,8 @@ struct TileReg {
 // zero-length (nothing is read, zeros are produced).
 #define TPL_TILE_ARGS_A(KT_)                                                                              \
   (A_K ? g.A + (int64_t)m0 * g.lda * 2 : g.A + (int64_t)(KT_) * 64 * g.lda * 2),                         \
-      ((KT_) * 64 < g.K ? (A_K ? (int64_t)(g.M - m0) * g.lda * 2 : (int64_t)(g.K - (KT_) * 64) * g.lda * 2) \
+      ((KT_) * 64 < g.K ? (A_K ? (int64_t)(g.M - m0) * g.lda * 2                                          \
+                               : (int64_t)(g.K - (KT_) * 64) * g.lda * 2 - g.a_trim)                      \
                         : 0),                                                                            \
       (A_K ? (KT_) * 128 : 0)
 #define TPL_TILE_ARGS_B(KT_)                                                                              \
@@ -514,7 +517,7 @@ struct CStage {
 };
 
 template <int BM, int BN, int WGM, int WGN, bool A_K, bool B_K, bool DMA, int EPI, typename TC>
-__global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
+__device__ __forceinline__ void gemm_bf16_body(Args g) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN, TM = WTM / 32, TN = WTN / 32;
   constexpr int kBOff = tile_bytes<BM, DMA>();                 // B tile offset in a stage
@@ -716,6 +719,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
       __syncthreads();
     }
   }
+}
+
+template <int BM, int BN, int WGM, int WGN, bool A_K, bool B_K, bool DMA, int EPI, typename TC>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
+  gemm_bf16_body<BM, BN, WGM, WGN, A_K, B_K, DMA, EPI, TC>(g);
+}
+
+// The same product as the first pass of a tail split (the last tile rows
+// split over K into fp32 partials); a symbol of its own so that a kernel
+// trace tells the two passes apart.
+template <int BM, int BN, int WGM, int WGN, bool A_K, bool B_K, bool DMA, int EPI, typename TC>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_tail_kernel(Args g) {
+  gemm_bf16_body<BM, BN, WGM, WGN, A_K, B_K, DMA, EPI, TC>(g);
 }
 
 // ------------------------------------------- multi-stage K pipeline (K-major operands)
@@ -1049,9 +1065,10 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(float* C, int64_t ldc, 
 
 struct SplitK { int splits, kchunk; };
 
-// C[m][n] (bf16) = ws[0][m][n] + ws[1][m][n] + ... in split order.
-__global__ __launch_bounds__(256) void splitk_sum_bf16_kernel(bf16* C, int64_t ldc, const float* __restrict__ ws,
-                                                              int nsplit, int M, int N) {
+// C[m][n] = ws[0][m][n] + ws[1][m][n] + ... in split order, stored as TC.
+template <typename TC>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(TC* C, int64_t ldc, const float* __restrict__ ws,
+                                                            int nsplit, int M, int N) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= (int64_t)M * N) return;
   const int64_t m = i / N, n = i % N;
@@ -1061,7 +1078,11 @@ __global__ __launch_bounds__(256) void splitk_sum_bf16_kernel(bf16* C, int64_t l
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += v[e];
   }
-  store4(C + m * ldc + n, acc[0], acc[1], acc[2], acc[3]);
+  if constexpr (sizeof(TC) == 2) {
+    store4(C + m * ldc + n, acc[0], acc[1], acc[2], acc[3]);
+  } else {
+    *reinterpret_cast<f32x4*>(C + m * ldc + n) = acc;
+  }
 }
 
 // Split of a bf16 data-gradient product (A K-major, B MN-major) whose
@@ -1098,6 +1119,47 @@ SplitK splitk_for(int dtype, int64_t M, int64_t N, int64_t K) {
   return r;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  static std::atomic<int> cache[64];
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Tail split of an fp32-output product on the 256x256 one-workgroup-per-CU
+// tile. When its tiles fill the CUs for r whole rounds and leave a short last
+// round (at most half the CUs busy for a whole tile's time), the tile rows of
+// that round run first instead, split over K so that they occupy the chip for
+// a fraction of a tile's time. Their fp32 partials live in the output rows
+// that the whole rounds write afterwards (no extra memory), and are summed in
+// split order (deterministic) into the tail rows before those rounds run.
+// row0 = first tail row (M when no split).
+struct TailSplit { int64_t row0; int splits, kchunk; };
+TailSplit tail_split_for(int64_t M, int64_t N, int64_t K, int cus) {
+  TailSplit t{M, 1, (int)K};
+  if (getenv("TPL_GEMM_TILE") || getenv("TPL_GEMM_NO_TAIL_SPLIT")) return t;
+  const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256, nblk = tm * tn;
+  if (nblk < cus) return t;
+  const int64_t rows_dp = (nblk / cus) * cus / tn;   // whole tile rows of the whole rounds
+  const int64_t tail = (tm - rows_dp) * tn;
+  if (tail == 0 || 2 * tail > cus) return t;
+  const int64_t tail_m = M - rows_dp * 256;
+  int64_t sp = std::min<int64_t>(cus / tail, K / 512);
+  sp = std::min<int64_t>(sp, rows_dp * 256 / tail_m);   // every partial fits in the rows written later
+  if (sp < 2) return t;
+  const int64_t chunk = ((K + sp - 1) / sp + 63) / 64 * 64;
+  t.row0 = rows_dp * 256;
+  t.splits = (int)((K + chunk - 1) / chunk);
+  t.kchunk = (int)chunk;
+  return t;
+}
+
 // ------------------------------------------------------------------ dispatch
 
 struct TileCfg { int bm, bn, variant; };
@@ -1106,7 +1168,7 @@ struct TileCfg { int bm, bn, variant; };
 
 template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BK_, int EPI, typename TC>
 hipError_t run(const GemmDesc& d, hipStream_t s) {
-  Args a;
+  Args a{};
   a.A = static_cast<const char*>(d.A); a.lda = d.lda;
   a.B = static_cast<const char*>(d.B); a.ldb = d.ldb;
   a.C = static_cast<char*>(d.C); a.ldc = d.ldc;
@@ -1149,7 +1211,7 @@ TileCfg choose_tile(int dtype, bool nt, int64_t M, int64_t N) {
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BK_, int EPI, typename TC>
 hipError_t run_v2(const GemmDesc& d, hipStream_t s) {
   constexpr bool kDma = AK && BK_;   // LDS-DMA for the forward products, register staging otherwise
-  Args a;
+  Args a{};
   a.A = static_cast<const char*>(d.A); a.lda = d.lda;
   a.B = static_cast<const char*>(d.B); a.ldb = d.ldb;
   a.C = static_cast<char*>(d.C); a.ldc = d.ldc;
@@ -1182,7 +1244,7 @@ hipError_t run_v2(const GemmDesc& d, hipStream_t s) {
 
 template <int BM, int BN, int WGM, int WGN, int NS, int OCC, int EPI, typename TC>
 hipError_t run_ms(const GemmDesc& d, hipStream_t s) {
-  Args a;
+  Args a{};
   a.A = static_cast<const char*>(d.A); a.lda = d.lda;
   a.B = static_cast<const char*>(d.B); a.ldb = d.ldb;
   a.C = static_cast<char*>(d.C); a.ldc = d.ldc;
@@ -1224,7 +1286,7 @@ hipError_t run_tiles(const GemmDesc& d, hipStream_t s) {
 // fp32 partial into the workspace (C = ws, splits s >= 1 at ws + s*M*N), then
 // one pass sums them in split order and rounds to bf16.
 hipError_t run_dgrad_split(const GemmDesc& d, const SplitK& sk, hipStream_t s) {
-  Args a;
+  Args a{};
   a.A = static_cast<const char*>(d.A); a.lda = d.lda;
   a.B = static_cast<const char*>(d.B); a.ldb = d.ldb;
   a.C = reinterpret_cast<char*>(d.ws); a.ldc = d.N;
@@ -1243,9 +1305,41 @@ hipError_t run_dgrad_split(const GemmDesc& d, const SplitK& sk, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t quads = (d.M * d.N + 3) / 4;
-  hipLaunchKernelGGL(splitk_sum_bf16_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(splitk_reduce_kernel<bf16>, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
                      static_cast<bf16*>(d.C), d.ldc, static_cast<const float*>(d.ws), a.splits, a.M, a.N);
   return hipGetLastError();
+}
+
+// Weight-gradient product (both operands MN-major, fp32 output, ldc == N)
+// with a tail split: the K-split pass over rows [row0, M) writes its partials
+// into C rows [0, splits*(M-row0)), the sum fills rows [row0, M), then the
+// whole rounds write rows [0, row0).
+hipError_t run_tn_tail(const GemmDesc& d, const TailSplit& t, hipStream_t s) {
+  const int64_t tail_m = d.M - t.row0;
+  Args a{};
+  a.A = static_cast<const char*>(d.A) + t.row0 * 2; a.lda = d.lda;
+  a.a_trim = t.row0 * 2;   // the view starts row0 columns in: its last row ends row0 columns early
+  a.B = static_cast<const char*>(d.B); a.ldb = d.ldb;
+  a.C = static_cast<char*>(d.C); a.ldc = d.N;
+  a.M = (int)tail_m; a.N = (int)d.N; a.K = (int)d.K;
+  a.tiles_m = (a.M + 255) / 256;
+  a.tiles_n = (a.N + 255) / 256;
+  a.splits = t.splits;
+  a.kchunk = t.kchunk;
+  a.ws = static_cast<float*>(d.C) + tail_m * d.N;
+  hipLaunchKernelGGL((gemm_bf16_tail_kernel<256, 256, 2, 4, false, false, false, EPI_NONE, float>),
+                     dim3(a.tiles_m * a.tiles_n * a.splits), dim3(512), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t quads = (tail_m * d.N + 3) / 4;
+  hipLaunchKernelGGL(splitk_reduce_kernel<float>, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
+                     static_cast<float*>(d.C) + t.row0 * d.ldc, d.ldc, static_cast<const float*>(d.C), t.splits,
+                     (int)tail_m, (int)d.N);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GemmDesc w = d;
+  w.M = t.row0;
+  return run_v2<256, 256, 2, 4, false, false, EPI_NONE, float>(w, s);
 }
 
 template <typename T>
@@ -1280,8 +1374,15 @@ hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
       default: return hipErrorInvalidValue;
     }
   }
-  if (!d.a_kmajor && !d.b_kmajor && d.c_f32 && d.epi == EPI_NONE)
+  if (!d.a_kmajor && !d.b_kmajor && d.c_f32 && d.epi == EPI_NONE) {
+    if constexpr (sizeof(T) == 2) {
+      if (d.ldc == d.N && choose_tile(d.dtype, false, d.M, d.N).variant == 1) {
+        const TailSplit t = tail_split_for(d.M, d.N, d.K, device_cus());
+        if (t.splits > 1) return run_tn_tail(d, t, s);
+      }
+    }
     return run_tiles<T, false, false, EPI_NONE, float>(d, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -68,3 +68,15 @@ def test_gemm_multistage(shape, monkeypatch):
     monkeypatch.setenv("TPL_GEMM_TILE", "256x256w8s4")
     M, N, K = shape
     test_gemm(("bf16", 1, 1, M, N, K, True))
+
+
+@pytest.mark.parametrize("shape", [(16600, 1000, 3000), (16640, 1024, 4096), (51200, 1024, 1024)],
+                         ids=lambda c: str(c))
+def test_gemm_tail_split(shape):
+    """fp32 weight-gradient products whose 256x256 tiles fill the CUs for whole
+    rounds and leave a short last round: those tile rows run first, split over
+    K, their partials parked in output rows that the whole rounds overwrite
+    (the output starts as NaN, so a row left unwritten fails). Ragged M, N and
+    K tails included."""
+    M, N, K = shape
+    test_gemm(("bf16", 0, 0, M, N, K, False))
