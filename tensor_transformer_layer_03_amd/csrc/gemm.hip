@@ -480,6 +480,31 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
 
+// Bias of a lane's output columns (TN blocks of 32 x 4 quads x 4 values,
+// the accumulator layout), loaded once per tile as packed bf16 pairs through
+// a buffer resource: columns at or past N read 0, so there is no branch and
+// every load is in flight at once.
+template <int TN>
+struct BiasCols {
+  u32x2 pk[TN][4];
+  __device__ __forceinline__ void load(const char* bias, int N, int ncol0, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the buffer-resource type exists only in the device pass
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(bias, (int64_t)N * 2);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        pk[j][q] = __builtin_amdgcn_raw_buffer_load_b64(rs, (ncol0 + j * 32 + 8 * q + 4 * (lane >> 5)) * 2, 0, 0);
+#endif
+  }
+  __device__ __forceinline__ void add(float* v, int j, int q) const {
+    v[0] += __builtin_bit_cast(float, pk[j][q][0] << 16);
+    v[1] += __builtin_bit_cast(float, pk[j][q][0] & 0xFFFF0000u);
+    v[2] += __builtin_bit_cast(float, pk[j][q][1] << 16);
+    v[3] += __builtin_bit_cast(float, pk[j][q][1] & 0xFFFF0000u);
+  }
+};
+
 // Output tile staged through LDS: the waves write their values (4
 // consecutive columns per lane and accumulator quad) into an LDS copy of the
 // tile's rows, 16-B chunks XOR-swizzled by row; then every thread copies whole
@@ -500,6 +525,38 @@ struct CStage {
       store4(reinterpret_cast<bf16*>(lds + off(r, c)), v[0], v[1], v[2], v[3]);
     } else {
       *reinterpret_cast<f32x4*>(lds + off(r, c)) = f32x4{v[0], v[1], v[2], v[3]};
+    }
+  }
+  __device__ __forceinline__ static void get4(const char* lds, int r, int c, float* v) {
+    static_assert(sizeof(TC) == 2, "bf16 tiles only");
+    load4(reinterpret_cast<const bf16*>(lds + off(r, c)), v);
+  }
+  // C2 rows m0.., columns n0.. -> staged rows [0, ROWS) (whole 16-B chunks of
+  // whole rows, all loads in flight before the LDS writes); out of range
+  // reads as 0
+  template <int ROWS>
+  __device__ __forceinline__ static void fill(char* lds, const char* src, int64_t ld, int m0, int n0, int M, int N,
+                                              int tid) {
+    constexpr int kPer = ROWS * kChunks / NT;
+    static_assert(kPer * NT == ROWS * kChunks, "staged rows do not split evenly over the threads");
+    constexpr int kBatch = kPer < 4 ? kPer : 4;
+#pragma unroll
+    for (int b0 = 0; b0 < kPer; b0 += kBatch) {
+      u32x4 v[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int idx = tid + (b0 + b) * NT;
+        const int r = idx / kChunks, ch = idx % kChunks;
+        const int m = m0 + r, n = n0 + ch * (16 / (int)sizeof(TC));
+        v[b] = u32x4{0u, 0u, 0u, 0u};
+        if (m < M && n < N) v[b] = *reinterpret_cast<const u32x4*>(src + ((int64_t)m * ld + n) * (int)sizeof(TC));
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int idx = tid + (b0 + b) * NT;
+        const int r = idx / kChunks, ch = idx % kChunks;
+        *reinterpret_cast<u32x4*>(lds + r * kRowBytes + ((ch ^ (r & kSwz)) << 4)) = v[b];
+      }
     }
   }
   // staged rows [0, rows) -> C rows m0.., columns n0..
@@ -669,38 +726,33 @@ __device__ __forceinline__ void gemm_bf16_body(Args g) {
   constexpr int kRP = kCap >= BM ? BM : (kCap >= 128 ? 128 : (kCap >= 64 ? 64 : 32));
   static_assert(kRP >= WTM && BM % kRP == 0 && kRP % WTM == 0, "staging rows must hold whole wave tiles");
   constexpr int kRounds = EPI == EPI_BIAS_GELU ? 2 : 1;   // u, then GeLU(u)
+  BiasCols<TN> bias;
+  if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias.load(g.bias, g.N, n0 + wn * WTN, lane);
   __syncthreads();
 #pragma unroll
   for (int round = 0; round < kRounds; ++round) {
 #pragma unroll
     for (int p = 0; p < BM / kRP; ++p) {
+      if constexpr (EPI == EPI_DGELU) {   // the pass's rows of u, staged where the results go
+        Stage::template fill<kRP>(smem, g.C2, g.ldc2, m0 + p * kRP, n0, g.M, g.N, (int)threadIdx.x);
+        __syncthreads();
+      }
       if ((wm * WTM) / kRP == p) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           const int rt = wm * WTM + i * 32 + (lane & 31);   // row within the tile
-          const int m = m0 + rt;
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int nt = wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
-              const int n = n0 + nt;
               float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-              if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
-                if (n < g.N) {
-                  float b[4];
-                  load4(reinterpret_cast<const bf16*>(g.bias) + n, b);
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) v[e] += b[e];
-                }
-              }
+              if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias.add(v, j, q);
               if constexpr (EPI == EPI_DGELU) {
-                if (m < g.M && n < g.N) {
-                  float u[4];
-                  load4(reinterpret_cast<const bf16*>(g.C2) + (int64_t)m * g.ldc2 + n, u);
+                float u[4];
+                Stage::get4(smem, rt - p * kRP, nt, u);
 #pragma unroll
-                  for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
-                }
+                for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
               }
               if constexpr (EPI == EPI_BIAS_GELU) {
                 if (round == 1) {
@@ -1008,6 +1060,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
   using Stage = CStage<TC, BN, NW * 64>;
   static_assert(NS * kStage >= BM * Stage::kRowBytes, "the stages must hold the staged tile");
   constexpr int kRounds = EPI == EPI_BIAS_GELU ? 2 : 1;   // u, then GeLU(u)
+  BiasCols<TN> bias;
+  if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias.load(g.bias, g.N, n0 + wn * WTN, lane);
   __syncthreads();
 #pragma unroll
   for (int round = 0; round < kRounds; ++round) {
@@ -1019,16 +1073,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int nt = wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
-          const int n = n0 + nt;
           float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) {
-            if (n < g.N) {
-              float b[4];
-              load4(reinterpret_cast<const bf16*>(g.bias) + n, b);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] += b[e];
-            }
-          }
+          if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias.add(v, j, q);
           if constexpr (EPI == EPI_BIAS_GELU) {
             if (round == 1) {
 #pragma unroll
@@ -1063,7 +1109,7 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(float* C, int64_t ldc, 
   *reinterpret_cast<f32x4*>(c) = acc;
 }
 
-struct SplitK { int splits, kchunk; };
+struct SplitK { int splits, kchunk, tile; };
 
 // C[m][n] = ws[0][m][n] + ws[1][m][n] + ... in split order, stored as TC.
 template <typename TC>
@@ -1090,28 +1136,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(TC* C, int64_t ldc, 
 // vocabulary): every split writes fp32 partials into the workspace, summed
 // and rounded once afterwards. Bounded by the workspace capacity.
 SplitK splitk_dgrad_for(int dtype, int64_t M, int64_t N, int64_t K, size_t ws_floats) {
-  SplitK r{1, (int)K};
+  SplitK r{1, (int)K, 0};
   if (dtype != DT_BF16 || getenv("TPL_GEMM_TILE") || M * N <= 0) return r;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles >= 384 || K < 8192) return r;
   int64_t sp = std::min<int64_t>((512 + tiles - 1) / tiles, K / 4096);
   sp = std::min<int64_t>(sp, (int64_t)(ws_floats / (size_t)(M * N)));
-  if (sp < 2) return r;
-  const int64_t chunk = ((K + sp - 1) / sp + 63) / 64 * 64;
-  r.splits = (int)((K + chunk - 1) / chunk);
-  r.kchunk = (int)chunk;
-  return r;
-}
-
-// Split of a weight-gradient product (both operands MN-major, fp32 output)
-// that takes the 128x128 tile: enough splits to put about two workgroups on
-// every CU, each split at least 1024 deep in K.
-SplitK splitk_for(int dtype, int64_t M, int64_t N, int64_t K) {
-  SplitK r{1, (int)K};
-  if (dtype != DT_BF16 || getenv("TPL_GEMM_TILE")) return r;
-  if (((M + 255) / 256) * ((N + 255) / 256) >= 384) return r;   // 256x256 tile, enough workgroups
-  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  int64_t sp = std::min<int64_t>(K / 1024, 512 / std::max<int64_t>(tiles, 1));
   if (sp < 2) return r;
   const int64_t chunk = ((K + sp - 1) / sp + 63) / 64 * 64;
   r.splits = (int)((K + chunk - 1) / chunk);
@@ -1130,6 +1160,34 @@ int device_cus() {
     cache[dev].store(v, std::memory_order_relaxed);
   }
   return v;
+}
+
+// Split of a weight-gradient product (both operands MN-major, fp32 output)
+// whose 256x256 grid is under a round of the CUs: the 256x256 tile with
+// enough splits for about one round (each at least 1024 deep in K, and at
+// least three quarters of the CUs busy), else the 128x128 tile with enough
+// splits for about two workgroups per CU (each at least 1024 deep). Split 0
+// writes C, the others the workspace, summed into C in split order. tile = 0:
+// no split.
+SplitK splitk_for(int dtype, int64_t M, int64_t N, int64_t K) {
+  SplitK r{1, (int)K, 0};
+  if (dtype != DT_BF16 || getenv("TPL_GEMM_TILE")) return r;
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (t256 >= 384 || t256 == 0) return r;   // 256x256 tile, enough workgroups
+  const int cus = device_cus();
+  int64_t sp = std::min<int64_t>(cus / t256, K / 1024);
+  int tile = 256;
+  if (sp < 2 || 4 * t256 * sp < 3 * cus) {
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    sp = std::min<int64_t>(K / 1024, 512 / std::max<int64_t>(tiles, 1));
+    tile = 128;
+  }
+  if (sp < 2) return r;
+  const int64_t chunk = ((K + sp - 1) / sp + 63) / 64 * 64;
+  r.splits = (int)((K + chunk - 1) / chunk);
+  r.kchunk = (int)chunk;
+  r.tile = tile;
+  return r;
 }
 
 // Tail split of an fp32-output product on the 256x256 one-workgroup-per-CU
@@ -1187,10 +1245,10 @@ hipError_t run(const GemmDesc& d, hipStream_t s) {
 // Tile choice (measured on MI355X over the layer's shapes): forward products
 // with at least 1024 tiles of 256x256 (the logits) take the four-stage 32-deep
 // K pipeline; otherwise the 256x256 tile with 8 waves when it yields at least
-// 384 workgroups (1.5 rounds over the 256 CUs), else 128x128 (two workgroups
-// per CU). TPL_GEMM_TILE=256x256[w8[t]] | 256x128[w8[t]] | 128x128 |
+// 384 workgroups (1.5 rounds over the 256 CUs; waves 4 x 2 for the GeLU
+// gradient epilogue, 2 x 4 otherwise), else 128x128 (two workgroups per CU). TPL_GEMM_TILE=256x256[w8[t]] | 256x128[w8[t]] | 128x128 |
 // 256x256w8s4 forces a shape (the tests use it to cover every tile path).
-TileCfg choose_tile(int dtype, bool nt, int64_t M, int64_t N) {
+TileCfg choose_tile(int dtype, bool nt, int64_t M, int64_t N, int epi = EPI_NONE) {
   if (dtype == DT_F32) return {128, 128, 0};
   if (const char* f = getenv("TPL_GEMM_TILE")) {
     if (!strcmp(f, "256x256")) return {256, 256, 0};
@@ -1204,7 +1262,7 @@ TileCfg choose_tile(int dtype, bool nt, int64_t M, int64_t N) {
   }
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
   if (nt && big >= 1024) return {256, 256, 5};
-  if (big >= 384) return {256, 256, 1};
+  if (big >= 384) return {256, 256, epi == EPI_DGELU ? 2 : 1};
   return {128, 128, 0};
 }
 
@@ -1223,11 +1281,13 @@ hipError_t run_v2(const GemmDesc& d, hipStream_t s) {
   a.splits = 1;
   a.kchunk = a.K;
   a.ws = nullptr;
-  if (!AK && !BK_ && d.c_f32 && d.ws && BM == 128 && BN == 128) {
+  if (!AK && !BK_ && d.c_f32 && d.ws && BM == BN) {
     const SplitK sk = splitk_for(d.dtype, d.M, d.N, d.K);
-    a.splits = sk.splits;
-    a.kchunk = sk.kchunk;
-    a.ws = d.ws;
+    if (sk.tile == BM) {
+      a.splits = sk.splits;
+      a.kchunk = sk.kchunk;
+      a.ws = d.ws;
+    }
   }
   const int nblk = a.tiles_m * a.tiles_n;
   if (nblk == 0) return hipSuccess;
@@ -1265,7 +1325,7 @@ hipError_t run_tiles(const GemmDesc& d, hipStream_t s) {
   if constexpr (sizeof(T) == 4) {
     return run<T, 128, 128, 2, 2, AK, BK_, EPI, TC>(d, s);
   } else {
-    const TileCfg t = choose_tile(d.dtype, AK && BK_, d.M, d.N);
+    const TileCfg t = choose_tile(d.dtype, AK && BK_, d.M, d.N, EPI);
     switch (t.variant) {
       case 1: return run_v2<256, 256, 2, 4, AK, BK_, EPI, TC>(d, s);
       case 2: return run_v2<256, 256, 4, 2, AK, BK_, EPI, TC>(d, s);
@@ -1376,6 +1436,8 @@ hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
   }
   if (!d.a_kmajor && !d.b_kmajor && d.c_f32 && d.epi == EPI_NONE) {
     if constexpr (sizeof(T) == 2) {
+      if (d.ws && splitk_for(d.dtype, d.M, d.N, d.K).tile == 256)
+        return run_v2<256, 256, 2, 4, false, false, EPI_NONE, float>(d, s);
       if (d.ldc == d.N && choose_tile(d.dtype, false, d.M, d.N).variant == 1) {
         const TailSplit t = tail_split_for(d.M, d.N, d.K, device_cus());
         if (t.splits > 1) return run_tn_tail(d, t, s);
