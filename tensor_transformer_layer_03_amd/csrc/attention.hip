@@ -620,7 +620,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3
   __shared__ __attribute__((aligned(16))) char sK[2][Tile::kBytes];
   __shared__ __attribute__((aligned(16))) char sV[2][Tile::kBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, grp = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
   // 1-D grid dealt heaviest query tiles first over all heads (causal tiles
   // differ up to seq/BQ-fold in work, so the last to start are the short ones)
   const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs;
@@ -694,13 +695,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
       const float m_new = fmaxf(m, mx);
       const float mc = m_new == -INFINITY ? 0.f : m_new * c;
-      const float alpha = exp2f(m * c - mc);
+      const float alpha = __builtin_amdgcn_exp2f(m * c - mc);
       float sum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(fmaf(sc[kt][r], c, -mc));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][r], c, -mc));
           sc[kt][r] = p;
           sum += p;
         }
@@ -745,7 +746,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) char sK[2][Tile::kBytes];
   __shared__ __attribute__((aligned(16))) char sV[2][Tile::kBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, grp = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
   // 1-D grid dealt heaviest query tiles first over all heads (causal tiles
   // differ up to seq/BQ-fold in work, so the last to start are the short ones)
   const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs;
@@ -817,7 +819,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(Args a) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = exp2f(fmaf(sc[kt][r], c, -lse_q));
+          float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][r], c, -lse_q));
           if (mask) {
             const int key = kv0 + 32 * kt + 16 * (r >> 3) + 8 * grp + (r & 7);
             if (key >= s || (CAUSAL && key > my_q) || my_q >= s) p = 0.f;
@@ -857,7 +859,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
   __shared__ __attribute__((aligned(16))) float sL[2][BQ];
   __shared__ __attribute__((aligned(16))) float sDl[2][BQ];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, grp = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
   // 1-D grid dealt heaviest key tiles (the first ones, under a causal mask) first over all heads
   const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs, kb = blockIdx.x / bhs;
   const int b = bh / a.heads, hd = bh % a.heads;
@@ -942,7 +945,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rq + e;
-            float p = exp2f(fmaf(sc[qt][r], c, -lq[e]));
+            float p = __builtin_amdgcn_exp2f(fmaf(sc[qt][r], c, -lq[e]));
             if (mask) {
               const int q = q0 + qo + e;
               if (q >= s || my_k >= s || (CAUSAL && my_k > q)) p = 0.f;
