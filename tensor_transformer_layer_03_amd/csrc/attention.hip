@@ -273,29 +273,37 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Args a) {
 }
 
 // ------------------------------------------------------------------ backward prologue
-// delta[b][h][q] = sum_d dO[q][d] * O[q][d]  (= sum_j P_qj dP_qj)
+// delta[b][h][q] = sum_d dO[q][d] * O[q][d]  (= sum_j P_qj dP_qj). A group of
+// G lanes takes one (token, head): lane j reads 16-B chunk j of O and dO, so
+// consecutive groups read consecutive stretches of a token's row (coalesced),
+// and the G partial dots are summed with lane shuffles in a fixed tree.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(Args a) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)a.batch * a.heads * a.seq;
-  if (idx >= total) return;
-  const int q = idx % a.seq;
-  const int hd = (idx / a.seq) % a.heads;
-  const int b = idx / ((int64_t)a.seq * a.heads);
-  const int64_t row = (int64_t)b * a.seq + q;
-  const T* o = reinterpret_cast<const T*>(a.ctx) + row * a.ld_ctx + hd * D;
-  const T* d = reinterpret_cast<const T*>(a.dctx) + row * a.ld_ctx + hd * D;
-  float acc = 0.f;
   constexpr int kVec = 16 / sizeof(T);
-#pragma unroll
-  for (int i = 0; i < D; i += kVec) {
+  constexpr int kChunks = D / kVec;   // 16-B chunks per (token, head)
+  constexpr int G = kChunks <= 8 ? 8 : (kChunks <= 16 ? 16 : 32);
+  static_assert(kChunks <= G && G <= kWave, "group does not fit a wave");
+  const int64_t gid = ((int64_t)blockIdx.x * 256 + threadIdx.x) / G;   // token row * heads + head
+  const int j = (int)(threadIdx.x % G);
+  const bool live = gid < (int64_t)a.batch * a.seq * a.heads;
+  const int64_t row = gid / a.heads;
+  const int hd = (int)(gid % a.heads);
+  float acc = 0.f;
+  if (live && j < kChunks) {
+    const T* o = reinterpret_cast<const T*>(a.ctx) + row * a.ld_ctx + hd * D + j * kVec;
+    const T* d = reinterpret_cast<const T*>(a.dctx) + row * a.ld_ctx + hd * D + j * kVec;
     Vec16<T> vo, vd;
-    vo.raw = ld16(o + i);
-    vd.raw = ld16(d + i);
+    vo.raw = ld16(o);
+    vd.raw = ld16(d);
 #pragma unroll
     for (int e = 0; e < kVec; ++e) acc += to_f32(vo.get(e)) * to_f32(vd.get(e));
   }
-  a.delta[idx] = acc;
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+  if (live && j == 0) {
+    const int64_t b = row / a.seq, q = row % a.seq;
+    a.delta[(b * a.heads + hd) * a.seq + q] = acc;
+  }
 }
 
 // ------------------------------------------------------------------ backward: dQ
@@ -1020,8 +1028,10 @@ hipError_t bwd_t(const AttnDesc& d, hipStream_t s) {
   Args a = make_args(d);
   {
     TraceScope trace(K_ATTN_BWD_PRE, s, (double)d.batch * d.seq * d.heads * d.head_dim * 2 * dtype_size(d.dtype));
-    const int64_t total = (int64_t)d.batch * d.heads * d.seq;
-    hipLaunchKernelGGL((attn_bwd_pre_kernel<T, D>), dim3((total + 255) / 256), dim3(256), 0, s, a);
+    constexpr int kChunks = D * (int)sizeof(T) / 16;
+    constexpr int G = kChunks <= 8 ? 8 : (kChunks <= 16 ? 16 : 32);
+    const int64_t lanes = (int64_t)d.batch * d.heads * d.seq * G;
+    hipLaunchKernelGGL((attn_bwd_pre_kernel<T, D>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

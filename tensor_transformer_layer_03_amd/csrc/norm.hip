@@ -219,6 +219,17 @@ __global__ __launch_bounds__(1024) void colsum_final_kernel(const float* __restr
   float s[4] = {0.f, 0.f, 0.f, 0.f};
   if (c < cols) {
     int i = wave;
+    for (; i + 240 < nchunks; i += 256) {   // four rounds of loads in flight, added in round order
+      float v[4][4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[it][u] = ws[((int64_t)(i + 64 * it + 16 * u) * nout + k) * cols + c];
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s[u] += v[it][u];
+    }
     for (; i + 48 < nchunks; i += 64) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) s[u] += ws[((int64_t)(i + 16 * u) * nout + k) * cols + c];

@@ -91,9 +91,15 @@ __global__ __launch_bounds__(1024) void xent_merge_kernel(const float* __restric
   const int t0 = wave * per, t1 = min(tcols, t0 + per);
   float m = -INFINITY, s = 0.f;
   if (row < rows) {
-    for (int t = t0; t < t1; ++t) {
-      const float2 p = *reinterpret_cast<const float2*>(xpart + ((int64_t)t * rows + row) * 2);
-      lse_merge(m, s, p.x, p.y);
+    constexpr int kB = 8;   // loads of a batch in flight together, then merged in order
+    for (int t = t0; t < t1; t += kB) {
+      float2 p[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (t + u < t1) p[u] = *reinterpret_cast<const float2*>(xpart + ((int64_t)(t + u) * rows + row) * 2);
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (t + u < t1) lse_merge(m, s, p[u].x, p[u].y);
     }
   }
   q[wave][lane][0] = m;
@@ -118,21 +124,52 @@ __global__ __launch_bounds__(1024) void xent_finish_kernel(StatPtrs st, int t, i
                                                            float* __restrict__ lse, float* __restrict__ loss_rows,
                                                            float* __restrict__ loss) {
   float acc = 0.f, cnt = 0.f;
-  for (int64_t r = threadIdx.x; r < rows; r += 1024) {
-    float M = -INFINITY;
-    for (int k = 0; k < t; ++k) M = fmaxf(M, st.p[k][r * 3]);
-    float S = 0.f, TL = 0.f;
+  constexpr int kB = 8;   // rows per thread whose loads are in flight together
+  for (int64_t r0 = threadIdx.x; r0 < rows; r0 += 1024 * kB) {
+    float M[kB], S[kB], TL[kB], w[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) { M[u] = -INFINITY; S[u] = 0.f; TL[u] = 0.f; w[u] = 0.f; }
     for (int k = 0; k < t; ++k) {
-      S += st.p[k][r * 3 + 1] * __expf(st.p[k][r * 3] - M);
-      TL += st.p[k][r * 3 + 2];
+      float mk[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int64_t r = r0 + 1024 * u;
+        mk[u] = r < rows ? st.p[k][r * 3] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) M[u] = fmaxf(M[u], mk[u]);
     }
-    const float l = M + __logf(S);
-    const float w = mask ? (float)mask[r] : 1.f;
-    const float lr = w * (l - TL);
-    lse[r] = l;
-    loss_rows[r] = lr;
-    acc += lr;
-    cnt += w;
+    for (int k = 0; k < t; ++k) {
+      float mk[kB], sk[kB], tk[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int64_t r = r0 + 1024 * u;
+        mk[u] = 0.f; sk[u] = 0.f; tk[u] = 0.f;
+        if (r < rows) { mk[u] = st.p[k][r * 3]; sk[u] = st.p[k][r * 3 + 1]; tk[u] = st.p[k][r * 3 + 2]; }
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        S[u] += sk[u] * __expf(mk[u] - M[u]);
+        TL[u] += tk[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int64_t r = r0 + 1024 * u;
+      if (r < rows) w[u] = mask ? (float)mask[r] : 1.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int64_t r = r0 + 1024 * u;
+      if (r < rows) {
+        const float l = M[u] + __logf(S[u]);
+        const float lr = w[u] * (l - TL[u]);
+        lse[r] = l;
+        loss_rows[r] = lr;
+        acc += lr;
+        cnt += w[u];
+      }
+    }
   }
   __shared__ float sa[16], sc[16];
   acc = wave_sum(acc);
