@@ -156,9 +156,9 @@ SOURCES = {"gemm": "gemm.hip", "attn": "attention.hip", "layernorm": "norm.hip",
            "partial": "norm.hip", "xent": "xent.hip", "embedding": "embedding.hip"}
 PROFILE_CMDS = {
     "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_c2 -o c2 -- "
-             "python3 <repo>/bench.py --steps 5 --warmup 2 --cpu-seqs 0",
+             "python3 <repo>/bench.py --steps 5 --warmup 2 --cpu-seqs 0 --no-layer-only",
     "pmc": "cd /tmp && rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <out>/pmc_<counter> -o bench "
-           "-- python3 <repo>/bench.py --steps 2 --warmup 1 --cpu-seqs 0 --trace-steps 1",
+           "-- python3 <repo>/bench.py --steps 2 --warmup 1 --cpu-seqs 0 --trace-steps 1 --no-layer-only",
     "copy": "cd /tmp && rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <out>/pmc_<counter> -o copy "
             "-- python3 <repo>/bench.py --copy-calibration",
 }
@@ -341,7 +341,8 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=-1,
                     help="sequences in the CPU-baseline sample (-1 = the whole micro-batch, 0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--layer-only", action="store_true", help="also time layer fwd+bwd without the loss")
+    ap.add_argument("--no-layer-only", dest="layer_only", action="store_false",
+                    help="skip the extra timing of the layer fwd+bwd without the loss")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 CSV output under DIR and exit")
     args = ap.parse_args()

@@ -14,7 +14,7 @@
 //  * gemm_kernel (fp32 storage): 128x128 tile, K-tile of 32 fp32 (128-B LDS
 //    rows), MN-major operands loaded as 8 k-rows x 16 B and transposed across
 //    lanes before the K-contiguous LDS store;
-//  * gemm_bf16_kernel: 256x256 (8 waves) or 128x128 (4 waves) tile, K-tile of
+//  * gemm_bf16_kernel: 256x256 or 256x192 (8 waves) or 128x128 (4 waves) tile, K-tile of
 //    64 bf16, two LDS stages; forward operands go straight to LDS
 //    (buffer_load ... lds), MN-major operands through registers into an
 //    [k][mn] LDS tile read with ds_read_b64_tr_b16; optional deterministic
@@ -515,7 +515,9 @@ template <typename TC, int BN, int NT>
 struct CStage {
   static constexpr int kRowBytes = BN * (int)sizeof(TC);
   static constexpr int kChunks = kRowBytes / 16;
-  static constexpr int kSwz = (kChunks < 32 ? kChunks : 32) - 1;
+  // XOR range: the largest power of two dividing the row's chunk count (at
+  // most 32), so a swizzled chunk stays inside its row
+  static constexpr int kSwz = ((kChunks & -kChunks) < 32 ? (kChunks & -kChunks) : 32) - 1;
   __device__ __forceinline__ static int off(int r, int c) {   // column c (a multiple of 4) of staged row r
     const int byte = c * (int)sizeof(TC);
     return r * kRowBytes + (((byte >> 4) ^ (r & kSwz)) << 4) + (byte & 15);
@@ -1246,8 +1248,10 @@ hipError_t run(const GemmDesc& d, hipStream_t s) {
 // with at least 1024 tiles of 256x256 (the logits) take the four-stage 32-deep
 // K pipeline; otherwise the 256x256 tile with 8 waves when it yields at least
 // 384 workgroups (1.5 rounds over the 256 CUs; waves 4 x 2 for the GeLU
-// gradient epilogue, 2 x 4 otherwise), else 128x128 (two workgroups per CU). TPL_GEMM_TILE=256x256[w8[t]] | 256x128[w8[t]] | 128x128 |
-// 256x256w8s4 forces a shape (the tests use it to cover every tile path).
+// gradient epilogue, 2 x 4 otherwise), else 128x128 (two workgroups per CU).
+// A forward product whose width is a multiple of 192 takes 256x192 tiles
+// (4 x 2 waves of 64x96) when their rounds finish sooner. TPL_GEMM_TILE=256x256[w8[t]] | 256x128[w8[t]] | 128x128 |
+// 256x256w8s4 | 256x192w8t forces a shape (the tests use it to cover every tile path).
 TileCfg choose_tile(int dtype, bool nt, int64_t M, int64_t N, int epi = EPI_NONE) {
   if (dtype == DT_F32) return {128, 128, 0};
   if (const char* f = getenv("TPL_GEMM_TILE")) {
@@ -1259,9 +1263,18 @@ TileCfg choose_tile(int dtype, bool nt, int64_t M, int64_t N, int epi = EPI_NONE
     if (!strcmp(f, "256x128w8t")) return {256, 128, 4};
     if (!strcmp(f, "128x128")) return {128, 128, 0};
     if (!strcmp(f, "256x256w8s4")) return {256, 256, nt ? 5 : 1};
+    if (!strcmp(f, "256x192w8t")) return nt ? TileCfg{256, 192, 6} : TileCfg{256, 256, 2};
   }
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
   if (nt && big >= 1024) return {256, 256, 5};
+  if (nt && big >= 384 && N % 192 == 0) {
+    // 256x192 tiles take 3/4 of a 256x256 tile's time: pick them when their
+    // rounds over the CUs finish sooner (QKV: 384 tiles = 2 rounds, 1.5 of
+    // them useful, vs 512 tiles of 192 = 2 rounds of 3/4)
+    const int64_t cus = device_cus();
+    const int64_t t192 = ((M + 255) / 256) * (N / 192);
+    if (3 * ((t192 + cus - 1) / cus) < 4 * ((big + cus - 1) / cus)) return {256, 192, 6};
+  }
   if (big >= 384) return {256, 256, epi == EPI_DGELU ? 2 : 1};
   return {128, 128, 0};
 }
@@ -1333,6 +1346,9 @@ hipError_t run_tiles(const GemmDesc& d, hipStream_t s) {
       case 4: return run_v2<256, 128, 4, 2, AK, BK_, EPI, TC>(d, s);
       case 5:
         if constexpr (AK && BK_) return run_ms<256, 256, 2, 4, 4, 2, EPI, TC>(d, s);
+        break;
+      case 6:   // forward products only (the MN-major layouts assume power-of-two tile widths)
+        if constexpr (AK && BK_) return run_v2<256, 192, 4, 2, AK, BK_, EPI, TC>(d, s);
         break;
       default: break;
     }

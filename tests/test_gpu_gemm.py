@@ -17,6 +17,8 @@ CASES = [
     ("bf16", 1, 1, 1024, 1024, 1024, False), ("bf16", 1, 1, 2048, 768, 520, True),
     ("bf16", 1, 0, 4096, 1024, 512, False), ("bf16", 0, 0, 1024, 512, 4000, False),
     ("bf16", 1, 1, 1, 8, 8, False), ("bf16", 0, 0, 8, 8, 1, False),
+    # width a multiple of 192 whose 256x256 grid leaves a half-empty last round: 256x192 tiles
+    ("bf16", 1, 1, 8000, 3072, 520, True),
 ]
 
 
@@ -50,7 +52,8 @@ def test_gemm(case):
 
 
 TILE_CASES = [(lay, tile) for lay in ((1, 1), (1, 0), (0, 0))
-              for tile in ("256x256", "256x256w8", "256x256w8t", "256x128", "256x128w8", "256x128w8t", "128x128", "256x256w8s4")]
+              for tile in ("256x256", "256x256w8", "256x256w8t", "256x128", "256x128w8", "256x128w8t", "128x128", "256x256w8s4",
+                           "256x192w8t")]
 
 
 @pytest.mark.parametrize("lay,tile", TILE_CASES, ids=lambda c: str(c))
