@@ -748,7 +748,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(Args a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attn_bwd_dq_bf16_kernel(Args a) {
   constexpr int NT = 256, BQ = 128, BKV = 64;
   using Tile = NatTile<D, NT>;
   __shared__ __attribute__((aligned(16))) char sK[2][Tile::kBytes];
@@ -808,41 +808,42 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(Args a) {
       vl.load(Vg, a.ld_qkv, kv0 + BKV, s, tid);
     }
     if (!CAUSAL || kv0 <= q0w + 31) {
-      f32x16 sc[2], dp[2];
+      const bool mask = (CAUSAL && kv0 + BKV - 1 > q0w) || kv0 + BKV > s || my_q >= s;
+      // the tile's two 32-key halves one after the other (half the score
+      // registers live at a time, so the accumulators stay in VGPRs)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+        f32x16 sc, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { sc[kt][r] = 0.f; dp[kt][r] = 0.f; }
+        for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
           Frag8<bf16> kf, vf;
           Tile::row_frag(kf, sK[cur], kt * 32 + krow, 2 * st + grp);
           Tile::row_frag(vf, sV[cur], kt * 32 + krow, 2 * st + grp);
-          mfma_step(sc[kt], kf, qf[st]);
-          mfma_step(dp[kt], vf, df[st]);
+          mfma_step(sc, kf, qf[st]);
+          mfma_step(dp, vf, df[st]);
         }
-      }
-      const bool mask = (CAUSAL && kv0 + BKV - 1 > q0w) || kv0 + BKV > s || my_q >= s;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][r], c, -lse_q));
+          float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lse_q));
           if (mask) {
             const int key = kv0 + 32 * kt + 16 * (r >> 3) + 8 * grp + (r & 7);
             if (key >= s || (CAUSAL && key > my_q) || my_q >= s) p = 0.f;
           }
-          sc[kt][r] = p * (dp[kt][r] - delta_q);   // dS^T
+          sc[r] = p * (dp[r] - delta_q);   // dS^T
         }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        Frag8<bf16> sf;
-        acc_frag(sf, sc[ks >> 1], 8 * (ks & 1));
+        for (int kh = 0; kh < 2; ++kh) {
+          const int ks = 2 * kt + kh;
+          Frag8<bf16> sf;
+          acc_frag(sf, sc, 8 * kh);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          Frag8<bf16> kf;
-          Tile::tr_frag(kf, sK[cur], ks * 16, dt * 32, lane);
-          mfma_step(dq[dt], kf, sf);
+          for (int dt = 0; dt < D / 32; ++dt) {
+            Frag8<bf16> kf;
+            Tile::tr_frag(kf, sK[cur], ks * 16, dt * 32, lane);
+            mfma_step(dq[dt], kf, sf);
+          }
         }
       }
     }
