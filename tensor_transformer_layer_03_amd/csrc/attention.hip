@@ -928,24 +928,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
       dl.load(dOg, a.ld_ctx, q0 + BQ, s, tid);
     }
     if (!CAUSAL || q0 + BQ - 1 >= k0w) {
-      f32x16 sc[2], dp[2];
+      const bool mask = (CAUSAL && q0 < k0w + 31) || q0 + BQ > s || my_k >= s;
+      // the tile's two 32-query halves one after the other (half the score
+      // registers live at a time)
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
+        f32x16 sc, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { sc[qt][r] = 0.f; dp[qt][r] = 0.f; }
+        for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
           Frag8<bf16> qf, df;
           Tile::row_frag(qf, sQ[cur], qt * 32 + qrow, 2 * st + grp);
           Tile::row_frag(df, sdO[cur], qt * 32 + qrow, 2 * st + grp);
-          mfma_step(sc[qt], qf, kf[st]);   // S[q][key], lane owns key
-          mfma_step(dp[qt], df, vf[st]);   // dP[q][key]
+          mfma_step(sc, qf, kf[st]);   // S[q][key], lane owns key
+          mfma_step(dp, df, vf[st]);   // dP[q][key]
         }
-      }
-      // query of accumulator element r of subtile qt: q0 + 32qt + 16(r/8) + 8grp + r%8
-      const bool mask = (CAUSAL && q0 < k0w + 31) || q0 + BQ > s || my_k >= s;
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+        // query of accumulator element r: q0 + 32qt + 16(r/8) + 8grp + r%8
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int qo = qt * 32 + 16 * (rq >> 1) + 8 * grp + 4 * (rq & 1);
@@ -954,27 +953,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rq + e;
-            float p = __builtin_amdgcn_exp2f(fmaf(sc[qt][r], c, -lq[e]));
+            float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lq[e]));
             if (mask) {
               const int q = q0 + qo + e;
               if (q >= s || my_k >= s || (CAUSAL && my_k > q)) p = 0.f;
             }
-            sc[qt][r] = p;                          // P
-            dp[qt][r] = p * (dp[qt][r] - dq[e]);    // dS
+            sc[r] = p;                       // P
+            dp[r] = p * (dp[r] - dq[e]);     // dS
           }
         }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        Frag8<bf16> pf, sf;
-        acc_frag(pf, sc[ks >> 1], 8 * (ks & 1));
-        acc_frag(sf, dp[ks >> 1], 8 * (ks & 1));
+        for (int kh = 0; kh < 2; ++kh) {
+          const int ks = 2 * qt + kh;
+          Frag8<bf16> pf, sf;
+          acc_frag(pf, sc, 8 * kh);
+          acc_frag(sf, dp, 8 * kh);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          Frag8<bf16> of, qf;
-          Tile::tr_frag(of, sdO[cur], ks * 16, dt * 32, lane);
-          Tile::tr_frag(qf, sQ[cur], ks * 16, dt * 32, lane);
-          mfma_step(dv[dt], of, pf);
-          mfma_step(dk[dt], qf, sf);
+          for (int dt = 0; dt < D / 32; ++dt) {
+            Frag8<bf16> of, qf;
+            Tile::tr_frag(of, sdO[cur], ks * 16, dt * 32, lane);
+            Tile::tr_frag(qf, sQ[cur], ks * 16, dt * 32, lane);
+            mfma_step(dv[dt], of, pf);
+            mfma_step(dk[dt], qf, sf);
+          }
         }
       }
     }
