@@ -144,6 +144,121 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(const T* __restrict__ dy, c
   }
 }
 
+// LayerNorm backward in one pass for rows of at most two 16-B chunks per lane
+// (hidden <= 1024 in bf16): a workgroup of eight waves takes one chunk of
+// kRowsPerChunk rows (wave w: rows w, w+8, w+16, w+24), loads all of its
+// rows' dsum, x and dy at once, writes dx for them (as ln_bwd_kernel) and the
+// chunk's column partials ws[chunk][k][c] (k = 0: sum of dsum * xhat, 1: sum
+// of dsum, 2: sum of dy, each wave over its rows in order, then the eight
+// wave sums in a fixed tree through LDS). One read of the three row tensors
+// instead of two.
+template <typename T>
+__global__ __launch_bounds__(512) void ln_bwd_fused_kernel(const T* dy, const T* __restrict__ dsum,
+                                                           const T* __restrict__ x, const float* __restrict__ mu,
+                                                           const float* __restrict__ rstd, const T* __restrict__ g,
+                                                           T* dx, float* __restrict__ ws, int64_t rows, int cols) {
+  constexpr int V = Vec16<T>::N, MAXC = 2, NW = 8, RPW = kRowsPerChunk / NW;
+  constexpr int kCols = 64 * MAXC * V;   // column slots of a workgroup
+  __shared__ float part[NW][3][kCols];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r0 = (int64_t)blockIdx.x * kRowsPerChunk;
+  const int nch = cols / V;
+
+  u32x4 rd[RPW][MAXC], rx[RPW][MAXC], ry[RPW][MAXC];
+  float m[RPW], rs[RPW];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int64_t row = r0 + wave + NW * j;
+    const bool live = row < rows;
+    m[j] = live ? mu[row] : 0.f;
+    rs[j] = live ? rstd[row] : 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int ch = lane + 64 * i;
+      rd[j][i] = rx[j][i] = ry[j][i] = u32x4{0u, 0u, 0u, 0u};
+      if (live && ch < nch) {
+        rd[j][i] = ld16(dsum + row * cols + ch * V);
+        rx[j][i] = ld16(x + row * cols + ch * V);
+        ry[j][i] = ld16(dy + row * cols + ch * V);
+      }
+    }
+  }
+  float gv[MAXC][V];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int ch = lane + 64 * i;
+    if (ch < nch) unpack<T>(ld16(g + ch * V), gv[i]);
+    else
+#pragma unroll
+      for (int e = 0; e < V; ++e) gv[i][e] = 0.f;
+  }
+  float a[3][MAXC][V];
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i)
+#pragma unroll
+      for (int e = 0; e < V; ++e) a[k][i][e] = 0.f;
+
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int64_t row = r0 + wave + NW * j;
+    if (row >= rows) break;   // uniform over the wave
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      float dv[V], xv[V], yv[V];
+      unpack<T>(rd[j][i], dv);
+      unpack<T>(rx[j][i], xv);
+      unpack<T>(ry[j][i], yv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float gd = dv[e] * gv[i][e];
+        s1 += gd;
+        s2 += gd * (xv[e] - m[j]) * rs[j];
+        a[0][i][e] += dv[e] * (xv[e] - m[j]) * rs[j];
+        a[1][i][e] += dv[e];
+        a[2][i][e] += yv[e];
+      }
+    }
+    const float mean1 = wave_sum(s1) / cols, mean2 = wave_sum(s2) / cols;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int ch = lane + 64 * i;
+      if (ch < nch) {
+        float dv[V], xv[V], yv[V];
+        unpack<T>(rd[j][i], dv);
+        unpack<T>(rx[j][i], xv);
+        unpack<T>(ry[j][i], yv);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const float xh = (xv[e] - m[j]) * rs[j];
+          yv[e] += rs[j] * (dv[e] * gv[i][e] - mean1 - xh * mean2);
+        }
+        st16(dx + row * cols + ch * V, pack<T>(yv));
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i)
+#pragma unroll
+      for (int e = 0; e < V; ++e) part[wave][k][(i * V + e) * 64 + lane] = a[k][i][e];
+  __syncthreads();
+  // slot q = (i*V + e)*64 + l holds column (l + 64 i)*V + e
+  for (int idx = threadIdx.x; idx < 3 * kCols; idx += 64 * NW) {
+    const int k = idx / kCols, q = idx % kCols;
+    const int l = q % 64, ie = q / 64, i = ie / V, e = ie % V;
+    const int c = (l + 64 * i) * V + e;
+    if (c < cols)
+      ws[((int64_t)blockIdx.x * 3 + k) * cols + c] =
+          ((part[0][k][q] + part[1][k][q]) + (part[2][k][q] + part[3][k][q])) +
+          ((part[4][k][q] + part[5][k][q]) + (part[6][k][q] + part[7][k][q]));
+  }
+}
+
 // Column partials. A workgroup covers 64 column chunks of 16 B and the
 // kRowsPerChunk rows of one row chunk; wave w takes rows w, w+4, ... and the
 // four wave sums are added in wave order through LDS, so every partial has a
@@ -349,6 +464,26 @@ hipError_t launch_layernorm_bwd(int dtype, const void* dy, const void* dsum, con
                                 const float* rstd, const void* g, void* dx, float* d_g, float* d_b,
                                 float* d_bout, float* ws, int64_t rows, int cols, hipStream_t s) {
   hipError_t e;
+  const int mc = maxc_for(dtype, cols);
+  if (mc > 0 && mc <= 2) {   // rows and column partials in one pass
+    {
+      TraceScope trace(K_LN_BWD, s, (double)rows * cols * 4 * dtype_size(dtype) + rows * 8.0);
+      const dim3 grid((unsigned)n_chunks(rows));
+      if (dtype == DT_BF16)
+        hipLaunchKernelGGL(ln_bwd_fused_kernel<bf16>, grid, dim3(512), 0, s, static_cast<const bf16*>(dy),
+                           static_cast<const bf16*>(dsum), static_cast<const bf16*>(x), mu, rstd,
+                           static_cast<const bf16*>(g), static_cast<bf16*>(dx), ws, rows, cols);
+      else
+        hipLaunchKernelGGL(ln_bwd_fused_kernel<float>, grid, dim3(512), 0, s, static_cast<const float*>(dy),
+                           static_cast<const float*>(dsum), static_cast<const float*>(x), mu, rstd,
+                           static_cast<const float*>(g), static_cast<float*>(dx), ws, rows, cols);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    TraceScope trace(K_COLSUM_FINAL, s);
+    hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64, 3), dim3(1024), 0, s, ws, (int)n_chunks(rows), cols,
+                       3, d_g, d_b, d_bout);
+    return hipGetLastError();
+  }
   {
     TraceScope trace(K_LN_BWD_COLS, s, (double)rows * cols * 3 * dtype_size(dtype));
     const int v = dtype == DT_BF16 ? 8 : 4;
