@@ -105,6 +105,7 @@ Saved saved_layout(const Dims& m, tpl_block block) {
     sz[S_ACT] = m.N * m.fr * es;
     sz[S_DU] = m.N * m.fr * es;
     ws = std::max(ws, colsum_ws_floats(m.N, m.fr));
+    ws = std::max(ws, (size_t)gemm_colpart_chunks(m.dt, m.N, m.fr) * m.fr);   // db_1 partials of the du product
     ws = std::max(ws, gemm_ws_floats(m.dt, m.h, m.fr, m.N));       // dW_2
     ws = std::max(ws, gemm_ws_floats(m.dt, m.fr, m.h, m.N));       // dW_1
   }
@@ -370,12 +371,16 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     void* u = slot<char>(saved, L, S_U);
     void* act = slot<char>(saved, L, S_ACT);
     void* du = slot<char>(saved, L, S_DU);
-    // du = (dy W_2) * GeLU'(u)
+    // du = (dy W_2) * GeLU'(u); db_1 = colsum(du) from the product's column
+    // partials when it provides them (bf16), else a separate pass below
     GemmDesc g = gemm(m, true, false, m.N, m.fr, m.h, dy, m.h, p->w_out, m.fr, du, m.fr);
     g.epi = EPI_DGELU;
     g.C2 = u;
     g.ldc2 = m.fr;
+    const int64_t cp = gemm_colpart_chunks(m.dt, m.N, m.fr);
+    if (cp > 0) g.colpart = ws;
     TPL_TRY(launch_gemm(g, s));
+    if (cp > 0) TPL_TRY(launch_colsum_final(ws, cp, m.fr, gr->d_b_in, s));
     GemmDesc g2 = gemm(m, false, false, m.h, m.fr, m.N, dy, m.h, act, m.fr, gr->d_w_out, m.fr);
     g2.c_f32 = true;
     g2.ws = ws;
@@ -384,7 +389,7 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     g1.c_f32 = true;
     g1.ws = ws;
     TPL_TRY(launch_gemm(g1, s));
-    TPL_TRY(launch_colsum(m.dt, du, m.fr, m.N, m.fr, gr->d_b_in, ws, s));
+    if (cp == 0) TPL_TRY(launch_colsum(m.dt, du, m.fr, m.N, m.fr, gr->d_b_in, ws, s));
     TPL_TRY(launch_gemm(gemm(m, true, false, m.N, m.h, m.fr, du, m.fr, p->w_in, m.h, d_ln_partial, m.h), s));
   }
   return TPL_OK;

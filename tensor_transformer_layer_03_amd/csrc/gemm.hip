@@ -58,6 +58,7 @@ struct Args {
   float* xpart;
   float* ws;       // split-K partials [splits-1][M][N] (split 0 writes C)
   int splits, kchunk;
+  float* colpart;  // EPI_DGELU: column sums of the output per half tile of rows (or NULL)
   int64_t a_trim;  // bytes of an MN-major A past its last row's M columns that are not the caller's
 };
 
@@ -768,6 +769,22 @@ __device__ __forceinline__ void gemm_bf16_body(Args g) {
         }
       }
       __syncthreads();
+      if constexpr (EPI == EPI_DGELU && sizeof(TC) == 2) {
+        // column sums of the staged (rounded) rows: thread t takes column
+        // t % BN over row block t / BN (kRC rows) of the tile, rows in order
+        constexpr int kH = NW * 64 / BN, kRC = BM / kH;
+        static_assert(kRP == BM && kH * BN == NW * 64 && kH * kRC == BM, "one staged pass, whole row blocks");
+        if (g.colpart) {
+          const int c = (int)threadIdx.x % BN, h = (int)threadIdx.x / BN;
+          const int rend = min(kRC, g.M - m0 - h * kRC);
+          if (rend > 0) {
+            float sum = 0.f;
+            for (int r = 0; r < rend; ++r)
+              sum += (float)*reinterpret_cast<const bf16*>(smem + Stage::off(h * kRC + r, c));
+            if (n0 + c < g.N) g.colpart[(int64_t)(m0 / kRC + h) * g.N + n0 + c] = sum;
+          }
+        }
+      }
       Stage::flush(smem, kRP, round == 0 ? g.C : g.C2, round == 0 ? g.ldc : g.ldc2, m0 + p * kRP, n0, g.M, g.N,
                    (int)threadIdx.x);
       __syncthreads();
@@ -1294,6 +1311,7 @@ hipError_t run_v2(const GemmDesc& d, hipStream_t s) {
   a.splits = 1;
   a.kchunk = a.K;
   a.ws = nullptr;
+  a.colpart = EPI == EPI_DGELU ? d.colpart : nullptr;
   if (!AK && !BK_ && d.c_f32 && d.ws && BM == BN) {
     const SplitK sk = splitk_for(d.dtype, d.M, d.N, d.K);
     if (sk.tile == BM) {
@@ -1476,6 +1494,13 @@ int xent_gemm_tile_cols(int dtype, int64_t M, int64_t N) {
 size_t gemm_ws_floats(int dtype, int64_t M, int64_t N, int64_t K) {
   const SplitK sk = splitk_for(dtype, M, N, K);
   return sk.splits > 1 ? (size_t)(sk.splits - 1) * (size_t)M * (size_t)N : 0;
+}
+int64_t gemm_colpart_chunks(int dtype, int64_t M, int64_t N) {
+  if (dtype != DT_BF16) return 0;   // the fp32 kernel takes no column partials
+  const TileCfg t = choose_tile(dtype, false, M, N, EPI_DGELU);
+  const int nt = (t.variant >= 1 && t.variant <= 4) ? 512 : 256;   // threads of the chosen workgroup
+  const int rc = t.bm / (nt / t.bn);                                  // rows per partial block
+  return (M + rc - 1) / rc;
 }
 size_t xent_part_floats(int64_t M, int64_t N) { return (size_t)((N + 127) / 128) * (size_t)M * 2; }
 

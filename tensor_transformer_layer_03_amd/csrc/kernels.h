@@ -53,11 +53,16 @@ struct GemmDesc {
   // EPI_XENT only: targets [M] (global ids), v0 = first vocabulary id of the
   // columns, xpart = per-tile (max, sum exp) [tile column][M][2]
   const int32_t* targets; int64_t v0; float* xpart;
+  // EPI_DGELU only (or NULL): column sums of the rounded output per block of
+  // half a tile's rows, [gemm_colpart_chunks()][N], blocks in row order
+  float* colpart;
 };
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
 // Floats of split-K workspace the product (M, N, K) with both operands MN-major
 // and an fp32 output takes (0: it is not split).
 size_t gemm_ws_floats(int dtype, int64_t M, int64_t N, int64_t K);
+// Row blocks of the column partials an EPI_DGELU product writes to colpart.
+int64_t gemm_colpart_chunks(int dtype, int64_t M, int64_t N);
 // Number of tile columns of the logits product with the fused statistics
 // epilogue (0: this shape/dtype takes the unfused path), and the floats of
 // per-tile statistics it needs at most.
@@ -92,6 +97,8 @@ size_t layernorm_bwd_ws_floats(int64_t rows, int cols);
 hipError_t launch_colsum(int dtype, const void* X, int64_t ld, int64_t rows, int cols, float* out,
                          float* ws, hipStream_t s);
 size_t colsum_ws_floats(int64_t rows, int cols);
+// out[c] = sum over chunks of ws[chunk][c] (fixed order).
+hipError_t launch_colsum_final(const float* ws, int64_t nchunks, int cols, float* out, hipStream_t s);
 hipError_t launch_partial_sum(int dtype, const void* const* parts, int n, const void* bias,
                               const void* residual, void* out, int64_t rows, int cols,
                               hipStream_t s);

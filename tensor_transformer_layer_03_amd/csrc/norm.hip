@@ -528,6 +528,13 @@ hipError_t launch_colsum(int dtype, const void* X, int64_t ld, int64_t rows, int
   return hipGetLastError();
 }
 
+hipError_t launch_colsum_final(const float* ws, int64_t nchunks, int cols, float* out, hipStream_t s) {
+  TraceScope trace(K_COLSUM_FINAL, s);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64, 1), dim3(1024), 0, s, ws, (int)nchunks, cols, 1, out,
+                     nullptr, nullptr);
+  return hipGetLastError();
+}
+
 hipError_t launch_partial_sum(int dtype, const void* const* parts, int n, const void* bias, const void* residual,
                               void* out, int64_t rows, int cols, hipStream_t s) {
   TraceScope trace(K_PARTIAL_SUM, s, (double)rows * cols * (n + 1 + (residual ? 1 : 0)) * dtype_size(dtype));
