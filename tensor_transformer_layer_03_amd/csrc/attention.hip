@@ -621,15 +621,20 @@ struct NatTile {
   }
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attn_fwd_bf16_kernel(Args a) {
-  constexpr int NT = 256, BQ = 128, BKV = 64;
+// SPL = 2 (used when the grid has under two waves per SIMD): eight waves, the
+// second four taking every other key tile of the same 128 queries; their
+// partial (O, max, sum) are merged at the end through LDS in a fixed order.
+template <int D, bool CAUSAL, int SPL>
+__global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL == 2 ? 2 : (D == 64 ? 3 : 1)))) void attn_fwd_bf16_kernel(Args a) {
+  constexpr int NT = 256 * SPL, BQ = 128, BKV = 64;
   using Tile = NatTile<D, NT>;
-  __shared__ __attribute__((aligned(16))) char sK[2][Tile::kBytes];
-  __shared__ __attribute__((aligned(16))) char sV[2][Tile::kBytes];
+  __shared__ __attribute__((aligned(16))) char sK[2][SPL][Tile::kBytes];
+  __shared__ __attribute__((aligned(16))) char sV[2][SPL][Tile::kBytes];
+  __shared__ float sML[SPL == 2 ? 2 * 256 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, grp = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
+  const int wave = wid & 3, par = wid >> 2;                     // query sub-tile, key-tile parity
   // 1-D grid dealt heaviest query tiles first over all heads (causal tiles
   // differ up to seq/BQ-fold in work, so the last to start are the short ones)
   const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs;
@@ -658,21 +663,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3
 
   const int kv_end = CAUSAL ? min(s, q0 + BQ) : s;
   const int ntiles = (kv_end + BKV - 1) / BKV;
-  Tile kl, vl;
-  kl.load(Kg, a.ld_qkv, 0, s, tid);
-  vl.load(Vg, a.ld_qkv, 0, s, tid);
-  kl.store(sK[0], tid);
-  vl.store(sV[0], tid);
+  const int nsteps = (ntiles + SPL - 1) / SPL;   // SPL key tiles per step, one per parity
+  Tile kl[SPL], vl[SPL];
+#pragma unroll
+  for (int u = 0; u < SPL; ++u) {
+    kl[u].load(Kg, a.ld_qkv, u * BKV, s, tid);
+    vl[u].load(Vg, a.ld_qkv, u * BKV, s, tid);
+    kl[u].store(sK[0][u], tid);
+    vl[u].store(sV[0][u], tid);
+  }
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1, kv0 = t * BKV;
-    const bool more = t + 1 < ntiles;
+  for (int t = 0; t < nsteps; ++t) {
+    const int cur = t & 1, kv0 = (t * SPL + par) * BKV;
+    const bool more = t + 1 < nsteps;
     if (more) {
-      kl.load(Kg, a.ld_qkv, kv0 + BKV, s, tid);
-      vl.load(Vg, a.ld_qkv, kv0 + BKV, s, tid);
+#pragma unroll
+      for (int u = 0; u < SPL; ++u) {
+        kl[u].load(Kg, a.ld_qkv, ((t + 1) * SPL + u) * BKV, s, tid);
+        vl[u].load(Vg, a.ld_qkv, ((t + 1) * SPL + u) * BKV, s, tid);
+      }
     }
-    if (!CAUSAL || kv0 <= q0w + 31) {
+    if (kv0 < kv_end && (!CAUSAL || kv0 <= q0w + 31)) {
+      const char* tK = sK[cur][par];
+      const char* tV = sV[cur][par];
       f32x16 sc[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -681,7 +695,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
           Frag8<bf16> kf;
-          Tile::row_frag(kf, sK[cur], kt * 32 + krow, 2 * st + grp);
+          Tile::row_frag(kf, tK, kt * 32 + krow, 2 * st + grp);
           mfma_step(sc[kt], kf, qf[st]);
         }
       }
@@ -727,16 +741,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
           Frag8<bf16> vf;
-          Tile::tr_frag(vf, sV[cur], ks * 16, dt * 32, lane);
+          Tile::tr_frag(vf, tV, ks * 16, dt * 32, lane);
           mfma_step(o[dt], vf, pf);
         }
       }
     }
     if (more) {
-      kl.store(sK[cur ^ 1], tid);
-      vl.store(sV[cur ^ 1], tid);
+#pragma unroll
+      for (int u = 0; u < SPL; ++u) {
+        kl[u].store(sK[cur ^ 1][u], tid);
+        vl[u].store(sV[cur ^ 1][u], tid);
+      }
     }
     __syncthreads();
+  }
+
+  if constexpr (SPL == 2) {
+    // the odd-parity wave of each query sub-tile hands (O, max, sum) to its
+    // partner through the free K stages: element e of lane i at [e][i]
+    static_assert(D / 2 * 256 * 4 <= (int)sizeof(sK), "the K stages must hold the exchanged O");
+    float* xo = reinterpret_cast<float*>(&sK[0][0][0]);
+    const int slot = wave * 64 + lane;
+    if (par == 1) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(dt * 16 + r) * 256 + slot] = o[dt][r];
+      sML[slot] = m;
+      sML[256 + slot] = l;
+    }
+    __syncthreads();
+    if (par == 1) return;
+    const float m1 = sML[slot], l1 = sML[256 + slot];
+    const float mn = fmaxf(m, m1);
+    const float mc = mn == -INFINITY ? 0.f : mn * c;
+    const float a0 = __builtin_amdgcn_exp2f(m * c - mc), a1 = __builtin_amdgcn_exp2f(m1 * c - mc);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] = o[dt][r] * a0 + xo[(dt * 16 + r) * 256 + slot] * a1;
+    l = l * a0 + l1 * a1;
+    m = mn;
   }
 
   if (my_q < s) {
@@ -747,15 +792,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3
   }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1))) void attn_bwd_dq_bf16_kernel(Args a) {
-  constexpr int NT = 256, BQ = 128, BKV = 64;
+// SPL = 2: eight waves, the second four taking every other key tile; the two
+// partial dQ are added at the end (even parity first).
+template <int D, bool CAUSAL, int SPL>
+__global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL == 2 ? 2 : (D == 64 ? 3 : 1)))) void attn_bwd_dq_bf16_kernel(Args a) {
+  constexpr int NT = 256 * SPL, BQ = 128, BKV = 64;
   using Tile = NatTile<D, NT>;
-  __shared__ __attribute__((aligned(16))) char sK[2][Tile::kBytes];
-  __shared__ __attribute__((aligned(16))) char sV[2][Tile::kBytes];
+  __shared__ __attribute__((aligned(16))) char sK[2][SPL][Tile::kBytes];
+  __shared__ __attribute__((aligned(16))) char sV[2][SPL][Tile::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, grp = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
+  const int wave = wid & 3, par = wid >> 2;                     // query sub-tile, key-tile parity
   // 1-D grid dealt heaviest query tiles first over all heads (causal tiles
   // differ up to seq/BQ-fold in work, so the last to start are the short ones)
   const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs;
@@ -793,21 +841,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3
 
   const int kv_end = CAUSAL ? min(s, q0 + BQ) : s;
   const int ntiles = (kv_end + BKV - 1) / BKV;
-  Tile kl, vl;
-  kl.load(Kg, a.ld_qkv, 0, s, tid);
-  vl.load(Vg, a.ld_qkv, 0, s, tid);
-  kl.store(sK[0], tid);
-  vl.store(sV[0], tid);
+  const int nsteps = (ntiles + SPL - 1) / SPL;   // SPL key tiles per step, one per parity
+  Tile kl[SPL], vl[SPL];
+#pragma unroll
+  for (int u = 0; u < SPL; ++u) {
+    kl[u].load(Kg, a.ld_qkv, u * BKV, s, tid);
+    vl[u].load(Vg, a.ld_qkv, u * BKV, s, tid);
+    kl[u].store(sK[0][u], tid);
+    vl[u].store(sV[0][u], tid);
+  }
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1, kv0 = t * BKV;
-    const bool more = t + 1 < ntiles;
+  for (int t = 0; t < nsteps; ++t) {
+    const int cur = t & 1, kv0 = (t * SPL + par) * BKV;
+    const bool more = t + 1 < nsteps;
     if (more) {
-      kl.load(Kg, a.ld_qkv, kv0 + BKV, s, tid);
-      vl.load(Vg, a.ld_qkv, kv0 + BKV, s, tid);
+#pragma unroll
+      for (int u = 0; u < SPL; ++u) {
+        kl[u].load(Kg, a.ld_qkv, ((t + 1) * SPL + u) * BKV, s, tid);
+        vl[u].load(Vg, a.ld_qkv, ((t + 1) * SPL + u) * BKV, s, tid);
+      }
     }
-    if (!CAUSAL || kv0 <= q0w + 31) {
+    if (kv0 < kv_end && (!CAUSAL || kv0 <= q0w + 31)) {
+      const char* tK = sK[cur][par];
+      const char* tV = sV[cur][par];
       const bool mask = (CAUSAL && kv0 + BKV - 1 > q0w) || kv0 + BKV > s || my_q >= s;
       // the tile's two 32-key halves one after the other (half the score
       // registers live at a time, so the accumulators stay in VGPRs)
@@ -819,8 +876,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
           Frag8<bf16> kf, vf;
-          Tile::row_frag(kf, sK[cur], kt * 32 + krow, 2 * st + grp);
-          Tile::row_frag(vf, sV[cur], kt * 32 + krow, 2 * st + grp);
+          Tile::row_frag(kf, tK, kt * 32 + krow, 2 * st + grp);
+          Tile::row_frag(vf, tV, kt * 32 + krow, 2 * st + grp);
           mfma_step(sc, kf, qf[st]);
           mfma_step(dp, vf, df[st]);
         }
@@ -841,17 +898,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) {
             Frag8<bf16> kf;
-            Tile::tr_frag(kf, sK[cur], ks * 16, dt * 32, lane);
+            Tile::tr_frag(kf, tK, ks * 16, dt * 32, lane);
             mfma_step(dq[dt], kf, sf);
           }
         }
       }
     }
     if (more) {
-      kl.store(sK[cur ^ 1], tid);
-      vl.store(sV[cur ^ 1], tid);
+#pragma unroll
+      for (int u = 0; u < SPL; ++u) {
+        kl[u].store(sK[cur ^ 1][u], tid);
+        vl[u].store(sV[cur ^ 1][u], tid);
+      }
     }
     __syncthreads();
+  }
+  if constexpr (SPL == 2) {
+    // odd-parity partial dQ through the free K stages: element e of lane i at [e][i]
+    static_assert(D / 2 * 256 * 4 <= (int)sizeof(sK), "the K stages must hold the exchanged dQ");
+    float* xq = reinterpret_cast<float*>(&sK[0][0][0]);
+    const int slot = wave * 64 + lane;
+    if (par == 1) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xq[(dt * 16 + r) * 256 + slot] = dq[dt][r];
+    }
+    __syncthreads();
+    if (par == 1) return;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[dt][r] += xq[(dt * 16 + r) * 256 + slot];
   }
   if (my_q < s) {
     bf16* dQg = reinterpret_cast<bf16*>(a.dqkv) + (int64_t)b * s * a.ld_qkv + hd * D;
@@ -859,17 +937,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3
   }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void attn_bwd_dkdv_bf16_kernel(Args a) {
-  constexpr int NT = 256, BKB = 128, BQ = 64;
+// SPL = 2: eight waves, the second four taking every other query tile; the
+// two partial dK and dV are added at the end (even parity first).
+template <int D, bool CAUSAL, int SPL>
+__global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL == 2 ? 2 : (D == 64 ? 2 : 1)))) void attn_bwd_dkdv_bf16_kernel(Args a) {
+  constexpr int NT = 256 * SPL, BKB = 128, BQ = 64;
   using Tile = NatTile<D, NT>;
-  __shared__ __attribute__((aligned(16))) char sQ[2][Tile::kBytes];
-  __shared__ __attribute__((aligned(16))) char sdO[2][Tile::kBytes];
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
-  __shared__ __attribute__((aligned(16))) float sDl[2][BQ];
+  __shared__ __attribute__((aligned(16))) char sQ[2][SPL][Tile::kBytes];
+  __shared__ __attribute__((aligned(16))) char sdO[2][SPL][Tile::kBytes];
+  __shared__ __attribute__((aligned(16))) float sL[2][SPL][BQ];
+  __shared__ __attribute__((aligned(16))) float sDl[2][SPL][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, grp = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
+  const int wave = wid & 3, par = wid >> 2;                     // key sub-tile, query-tile parity
   // 1-D grid dealt heaviest key tiles (the first ones, under a causal mask) first over all heads
   const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs, kb = blockIdx.x / bhs;
   const int b = bh / a.heads, hd = bh % a.heads;
@@ -903,31 +984,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
 
   const int qs = CAUSAL ? (k0 / BQ) * BQ : 0;
   const int ntiles = s > qs ? (s - qs + BQ - 1) / BQ : 0;
-  Tile ql, dl;
+  const int nsteps = (ntiles + SPL - 1) / SPL;   // SPL query tiles per step, one per parity
+  Tile ql[SPL], dl[SPL];
+  // statistics of the SPL query tiles from q0 (rows past the sequence read 0)
   auto stage_stats = [&](int buf, int q0) {
-    if (tid < BQ) {
-      const int q = q0 + tid;
-      sL[buf][tid] = q < s ? a.lse[stat + q] * kLog2e : 0.f;
-      sDl[buf][tid] = q < s ? a.delta[stat + q] : 0.f;
+    if (tid < BQ * SPL) {
+      const int u = tid / BQ, j = tid % BQ, q = q0 + u * BQ + j;
+      sL[buf][u][j] = q < s ? a.lse[stat + q] * kLog2e : 0.f;
+      sDl[buf][u][j] = q < s ? a.delta[stat + q] : 0.f;
     }
   };
   if (ntiles > 0) {
-    ql.load(Qg, a.ld_qkv, qs, s, tid);
-    dl.load(dOg, a.ld_ctx, qs, s, tid);
-    ql.store(sQ[0], tid);
-    dl.store(sdO[0], tid);
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      ql[u].load(Qg, a.ld_qkv, qs + u * BQ, s, tid);
+      dl[u].load(dOg, a.ld_ctx, qs + u * BQ, s, tid);
+      ql[u].store(sQ[0][u], tid);
+      dl[u].store(sdO[0][u], tid);
+    }
     stage_stats(0, qs);
   }
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1, q0 = qs + t * BQ;
-    const bool more = t + 1 < ntiles;
+  for (int t = 0; t < nsteps; ++t) {
+    const int cur = t & 1, q0 = qs + (t * SPL + par) * BQ;
+    const bool more = t + 1 < nsteps;
     if (more) {
-      ql.load(Qg, a.ld_qkv, q0 + BQ, s, tid);
-      dl.load(dOg, a.ld_ctx, q0 + BQ, s, tid);
+#pragma unroll
+      for (int u = 0; u < SPL; ++u) {
+        ql[u].load(Qg, a.ld_qkv, qs + ((t + 1) * SPL + u) * BQ, s, tid);
+        dl[u].load(dOg, a.ld_ctx, qs + ((t + 1) * SPL + u) * BQ, s, tid);
+      }
     }
-    if (!CAUSAL || q0 + BQ - 1 >= k0w) {
+    if (q0 < s && (!CAUSAL || q0 + BQ - 1 >= k0w)) {
+      const char* tQ = sQ[cur][par];
+      const char* tdO = sdO[cur][par];
+      const float* tL = sL[cur][par];
+      const float* tDl = sDl[cur][par];
       const bool mask = (CAUSAL && q0 < k0w + 31) || q0 + BQ > s || my_k >= s;
       // the tile's two 32-query halves one after the other (half the score
       // registers live at a time)
@@ -939,8 +1032,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
           Frag8<bf16> qf, df;
-          Tile::row_frag(qf, sQ[cur], qt * 32 + qrow, 2 * st + grp);
-          Tile::row_frag(df, sdO[cur], qt * 32 + qrow, 2 * st + grp);
+          Tile::row_frag(qf, tQ, qt * 32 + qrow, 2 * st + grp);
+          Tile::row_frag(df, tdO, qt * 32 + qrow, 2 * st + grp);
           mfma_step(sc, qf, kf[st]);   // S[q][key], lane owns key
           mfma_step(dp, df, vf[st]);   // dP[q][key]
         }
@@ -948,8 +1041,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int qo = qt * 32 + 16 * (rq >> 1) + 8 * grp + 4 * (rq & 1);
-          const f32x4 lq = *reinterpret_cast<const f32x4*>(&sL[cur][qo]);
-          const f32x4 dq = *reinterpret_cast<const f32x4*>(&sDl[cur][qo]);
+          const f32x4 lq = *reinterpret_cast<const f32x4*>(&tL[qo]);
+          const f32x4 dq = *reinterpret_cast<const f32x4*>(&tDl[qo]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rq + e;
@@ -971,8 +1064,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) {
             Frag8<bf16> of, qf;
-            Tile::tr_frag(of, sdO[cur], ks * 16, dt * 32, lane);
-            Tile::tr_frag(qf, sQ[cur], ks * 16, dt * 32, lane);
+            Tile::tr_frag(of, tdO, ks * 16, dt * 32, lane);
+            Tile::tr_frag(qf, tQ, ks * 16, dt * 32, lane);
             mfma_step(dv[dt], of, pf);
             mfma_step(dk[dt], qf, sf);
           }
@@ -980,11 +1073,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
       }
     }
     if (more) {
-      ql.store(sQ[cur ^ 1], tid);
-      dl.store(sdO[cur ^ 1], tid);
-      stage_stats(cur ^ 1, q0 + BQ);
+#pragma unroll
+      for (int u = 0; u < SPL; ++u) {
+        ql[u].store(sQ[cur ^ 1][u], tid);
+        dl[u].store(sdO[cur ^ 1][u], tid);
+      }
+      stage_stats(cur ^ 1, qs + (t + 1) * SPL * BQ);
     }
     __syncthreads();
+  }
+  if constexpr (SPL == 2) {
+    // odd-parity partial dK (through the free Q stages) and dV (through the
+    // dO stages): element e of lane i at [e][i]
+    static_assert(D / 2 * 256 * 4 <= (int)sizeof(sQ), "the Q stages must hold the exchanged dK");
+    float* xk = reinterpret_cast<float*>(&sQ[0][0][0]);
+    float* xv = reinterpret_cast<float*>(&sdO[0][0][0]);
+    const int slot = wave * 64 + lane;
+    if (par == 1) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          xk[(dt * 16 + r) * 256 + slot] = dk[dt][r];
+          xv[(dt * 16 + r) * 256 + slot] = dv[dt][r];
+        }
+    }
+    __syncthreads();
+    if (par == 1) return;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[dt][r] += xk[(dt * 16 + r) * 256 + slot];
+        dv[dt][r] += xv[(dt * 16 + r) * 256 + slot];
+      }
   }
   if (my_k < s) {
     bf16* dKg = reinterpret_cast<bf16*>(a.dqkv) + (int64_t)b * s * a.ld_qkv + hr + hd * D;
@@ -997,6 +1119,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
 double attn_pairs(const AttnDesc& d) {
   const double s = d.seq;
   return (double)d.batch * d.heads * (d.causal ? s * (s + 1) / 2 : s * s);
+}
+
+// The eight-wave form (tiles of the looped axis dealt over two wave groups)
+// when the four-wave grid would leave fewer than two waves per SIMD of the
+// chip: each workgroup of 128 rows then has twice the waves in flight.
+bool attn_split(const AttnDesc& d) {
+  if (const char* f = getenv("TPL_ATTN_SPLIT")) return atoi(f) != 0;
+  const int64_t waves = (int64_t)((d.seq + 127) / 128) * d.batch * d.heads * 4;
+  return waves < 2 * 4 * (int64_t)device_cu_count();
 }
 
 Args make_args(const AttnDesc& d) {
@@ -1016,8 +1147,13 @@ hipError_t fwd_t(const AttnDesc& d, hipStream_t s) {
   Args a = make_args(d);
   dim3 grid((unsigned)(((d.seq + 127) / 128) * d.batch * d.heads));
   if constexpr (sizeof(T) == 2) {
-    if (d.causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), grid, dim3(256), 0, s, a);
+    if (attn_split(d)) {
+      if (d.causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, 2>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, 2>), grid, dim3(512), 0, s, a);
+    } else {
+      if (d.causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, 1>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, 1>), grid, dim3(256), 0, s, a);
+    }
   } else {
     if (d.causal) hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((attn_fwd_kernel<T, D, false>), grid, dim3(256), 0, s, a);
@@ -1041,8 +1177,16 @@ hipError_t bwd_t(const AttnDesc& d, hipStream_t s) {
   {
     TraceScope trace(K_ATTN_BWD_DKDV, s, 6.0 * attn_pairs(d) * d.head_dim);   // dV, dP, dK
     if constexpr (sizeof(T) == 2) {
-      if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false>), grid, dim3(256), 0, s, a);
+      // eight waves only at head size 64: with 96 or 128 the dK, dV, K and V
+      // registers of two waves per SIMD exceed the register file (spills)
+      constexpr int kSpl = D == 64 ? 2 : 1;
+      if (kSpl == 2 && attn_split(d)) {
+        if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, kSpl>), grid, dim3(256 * kSpl), 0, s, a);
+        else hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false, kSpl>), grid, dim3(256 * kSpl), 0, s, a);
+      } else {
+        if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, 1>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false, 1>), grid, dim3(256), 0, s, a);
+      }
     } else {
       if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true>), grid, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, false>), grid, dim3(256), 0, s, a);
@@ -1052,8 +1196,13 @@ hipError_t bwd_t(const AttnDesc& d, hipStream_t s) {
   }
   TraceScope trace(K_ATTN_BWD_DQ, s, 2.0 * attn_pairs(d) * d.head_dim);     // dQ
   if constexpr (sizeof(T) == 2) {
-    if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false>), grid, dim3(256), 0, s, a);
+    if (attn_split(d)) {
+      if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, 2>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false, 2>), grid, dim3(512), 0, s, a);
+    } else {
+      if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, 1>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false, 1>), grid, dim3(256), 0, s, a);
+    }
   } else {
     if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, false>), grid, dim3(256), 0, s, a);

@@ -1261,15 +1261,26 @@ hipError_t run(const GemmDesc& d, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile choice (measured on MI355X over the layer's shapes): forward products
-// with at least 1024 tiles of 256x256 (the logits) take the four-stage 32-deep
-// K pipeline; otherwise the 256x256 tile with 8 waves when it yields at least
-// 384 workgroups (1.5 rounds over the 256 CUs; waves 4 x 2 for the GeLU
-// gradient epilogue, 2 x 4 otherwise), else 128x128 (two workgroups per CU).
-// A forward product whose width is a multiple of 192 takes 256x192 tiles
-// (4 x 2 waves of 64x96) when their rounds finish sooner. TPL_GEMM_TILE=256x256[w8[t]] | 256x128[w8[t]] | 128x128 |
-// 256x256w8s4 | 256x192w8t forces a shape (the tests use it to cover every tile path).
-TileCfg choose_tile(int dtype, bool nt, int64_t M, int64_t N, int epi = EPI_NONE) {
+// Tile choice. Forward products with at least 1024 tiles of 256x256 (the
+// logits) take the four-stage 32-deep K pipeline. Other forward (NT) and
+// activation-gradient (NN) products take the candidate with the least
+//   rounds x (tile area x workgroups per CU) / throughput,
+// rounds = ceil(tiles / (workgroups per CU x CUs)): a partly filled last round
+// costs a whole one. Relative per-CU throughputs, fitted to timings of every
+// forward and gradient product of the four bf16 layer shards on MI355X:
+// 256x256 (8 waves, one workgroup per CU) 1.0; 256x192 (forward only) 0.8;
+// 128x128 (4 waves, two per CU) 0.7 forward, 0.8 gradient. (256x128 won some
+// gradient products timed alone but lost inside the layer pass, where the
+// operands arrive from the previous kernels instead of a warm cache.) The
+// 256x256 tile runs as 2 x 4 waves of 128x64 for forward products and 4 x 2
+// waves of 64x128 for gradient products (faster there by up to 14% in the
+// same timings). Weight-gradient (TN) products keep 256x256 with 2 x 4 waves
+// when that gives at least 384 workgroups, else 128x128 (the split-K and
+// tail-split paths decide their own tiles).
+// TPL_GEMM_TILE=256x256[w8[t]] | 256x128[w8[t]] | 128x128 | 256x256w8s4 |
+// 256x192w8t forces a shape (the tests use it to cover every tile path).
+TileCfg choose_tile(int dtype, bool ak, bool bk, int64_t M, int64_t N, int epi = EPI_NONE) {
+  const bool nt = ak && bk;
   if (dtype == DT_F32) return {128, 128, 0};
   if (const char* f = getenv("TPL_GEMM_TILE")) {
     if (!strcmp(f, "256x256")) return {256, 256, 0};
@@ -1283,17 +1294,34 @@ TileCfg choose_tile(int dtype, bool nt, int64_t M, int64_t N, int epi = EPI_NONE
     if (!strcmp(f, "256x192w8t")) return nt ? TileCfg{256, 192, 6} : TileCfg{256, 256, 2};
   }
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  if (!ak && !bk) return big >= 384 ? TileCfg{256, 256, 1} : TileCfg{128, 128, 0};
   if (nt && big >= 1024) return {256, 256, 5};
-  if (nt && big >= 384 && N % 192 == 0) {
-    // 256x192 tiles take 3/4 of a 256x256 tile's time: pick them when their
-    // rounds over the CUs finish sooner (QKV: 384 tiles = 2 rounds, 1.5 of
-    // them useful, vs 512 tiles of 192 = 2 rounds of 3/4)
-    const int64_t cus = device_cus();
-    const int64_t t192 = ((M + 255) / 256) * (N / 192);
-    if (3 * ((t192 + cus - 1) / cus) < 4 * ((big + cus - 1) / cus)) return {256, 192, 6};
+  struct Cand { TileCfg t; int per_cu; double thr; };
+  const int64_t cus = device_cus();
+  (void)epi;
+  Cand cands[3];
+  int nc = 0;
+  if (nt) {
+    cands[nc++] = {{256, 256, 1}, 1, 1.0};
+    cands[nc++] = {{256, 192, 6}, 1, 0.8};
+    cands[nc++] = {{128, 128, 0}, 2, 0.7};
+  } else {
+    cands[nc++] = {{256, 256, 2}, 1, 1.0};
+    cands[nc++] = {{128, 128, 0}, 2, 0.8};
   }
-  if (big >= 384) return {256, 256, epi == EPI_DGELU ? 2 : 1};
-  return {128, 128, 0};
+  TileCfg best = cands[0].t;
+  double best_cost = 0.0;
+  for (int i = 0; i < nc; ++i) {
+    const Cand& c = cands[i];
+    const int64_t tiles = ((M + c.t.bm - 1) / c.t.bm) * ((N + c.t.bn - 1) / c.t.bn);
+    const int64_t rounds = (tiles + c.per_cu * cus - 1) / (c.per_cu * cus);
+    const double cost = (double)rounds * c.t.bm * c.t.bn * c.per_cu / c.thr;
+    if (i == 0 || cost < best_cost) {
+      best = c.t;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 template <int BM, int BN, int WGM, int WGN, bool AK, bool BK_, int EPI, typename TC>
@@ -1356,7 +1384,7 @@ hipError_t run_tiles(const GemmDesc& d, hipStream_t s) {
   if constexpr (sizeof(T) == 4) {
     return run<T, 128, 128, 2, 2, AK, BK_, EPI, TC>(d, s);
   } else {
-    const TileCfg t = choose_tile(d.dtype, AK && BK_, d.M, d.N, EPI);
+    const TileCfg t = choose_tile(d.dtype, AK, BK_, d.M, d.N, EPI);
     switch (t.variant) {
       case 1: return run_v2<256, 256, 2, 4, AK, BK_, EPI, TC>(d, s);
       case 2: return run_v2<256, 256, 4, 2, AK, BK_, EPI, TC>(d, s);
@@ -1472,7 +1500,7 @@ hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     if constexpr (sizeof(T) == 2) {
       if (d.ws && splitk_for(d.dtype, d.M, d.N, d.K).tile == 256)
         return run_v2<256, 256, 2, 4, false, false, EPI_NONE, float>(d, s);
-      if (d.ldc == d.N && choose_tile(d.dtype, false, d.M, d.N).variant == 1) {
+      if (d.ldc == d.N && choose_tile(d.dtype, false, false, d.M, d.N).variant == 1) {
         const TailSplit t = tail_split_for(d.M, d.N, d.K, device_cus());
         if (t.splits > 1) return run_tn_tail(d, t, s);
       }
@@ -1497,12 +1525,14 @@ size_t gemm_ws_floats(int dtype, int64_t M, int64_t N, int64_t K) {
 }
 int64_t gemm_colpart_chunks(int dtype, int64_t M, int64_t N) {
   if (dtype != DT_BF16) return 0;   // the fp32 kernel takes no column partials
-  const TileCfg t = choose_tile(dtype, false, M, N, EPI_DGELU);
+  const TileCfg t = choose_tile(dtype, true, false, M, N, EPI_DGELU);
   const int nt = (t.variant >= 1 && t.variant <= 4) ? 512 : 256;   // threads of the chosen workgroup
   const int rc = t.bm / (nt / t.bn);                                  // rows per partial block
   return (M + rc - 1) / rc;
 }
 size_t xent_part_floats(int64_t M, int64_t N) { return (size_t)((N + 127) / 128) * (size_t)M * 2; }
+
+int device_cu_count() { return device_cus(); }
 
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s) {
   TraceScope trace(d.a_kmajor && d.b_kmajor ? K_GEMM_NT : (d.a_kmajor ? K_GEMM_NN : K_GEMM_TN), s,

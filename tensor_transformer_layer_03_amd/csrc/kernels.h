@@ -67,6 +67,8 @@ int64_t gemm_colpart_chunks(int dtype, int64_t M, int64_t N);
 // epilogue (0: this shape/dtype takes the unfused path), and the floats of
 // per-tile statistics it needs at most.
 int xent_gemm_tile_cols(int dtype, int64_t M, int64_t N);
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cu_count();
 size_t xent_part_floats(int64_t M, int64_t N);
 
 // ------------------------------------------------------------------ attention

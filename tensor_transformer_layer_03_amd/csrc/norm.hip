@@ -45,13 +45,19 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const T* __restrict__ x, co
   if (row >= rows) return;
   const int nch = cols / V;
   const T* xr = x + row * cols;
-  u32x4 cache[MAXC];
+  u32x4 cache[MAXC], gcache[MAXC], bcache[MAXC];
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
+  for (int i = 0; i < MAXC; ++i) {   // gamma and beta are loaded with the row, ahead of the reductions
     const int ch = lane + 64 * i;
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (ch < nch) raw = ld16(xr + ch * V);
+    u32x4 raw = {0u, 0u, 0u, 0u}, rg = raw, rb = raw;
+    if (ch < nch) {
+      raw = ld16(xr + ch * V);
+      rg = ld16(g + ch * V);
+      rb = ld16(bta + ch * V);
+    }
+    gcache[i] = rg;
+    bcache[i] = rb;
     cache[i] = raw;
     float v[V];
     unpack<T>(raw, v);
@@ -78,8 +84,8 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const T* __restrict__ x, co
     if (ch < nch) {
       float v[V], gv[V], bv[V];
       unpack<T>(cache[i], v);
-      unpack<T>(ld16(g + ch * V), gv);
-      unpack<T>(ld16(bta + ch * V), bv);
+      unpack<T>(gcache[i], gv);
+      unpack<T>(bcache[i], bv);
 #pragma unroll
       for (int e = 0; e < V; ++e) v[e] = (v[e] - mean) * rstd * gv[e] + bv[e];
       st16(yr + ch * V, pack<T>(v));
@@ -377,23 +383,35 @@ __global__ __launch_bounds__(256) void partial_sum_kernel(PartPtrs parts, int n,
   const int64_t row = i / (cols / V);
   const int col = (int)(i % (cols / V)) * V;
   const int64_t off = row * cols + col;
+  // every load is issued before the first add (n <= 16 partials), then the
+  // values are added in the fixed order residual, bias, partials 0..n-1
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const u32x4 rres = residual ? ld16(residual + off) : zero;
+  const u32x4 rbias = bias ? ld16(bias + col) : zero;
+  u32x4 raw[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (k < n) raw[k] = ld16(static_cast<const T*>(parts.p[k]) + off);
   float acc[V], t[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) acc[e] = 0.f;
   if (residual) {
-    unpack<T>(ld16(residual + off), t);
+    unpack<T>(rres, t);
 #pragma unroll
     for (int e = 0; e < V; ++e) acc[e] += t[e];
   }
   if (bias) {
-    unpack<T>(ld16(bias + col), t);
+    unpack<T>(rbias, t);
 #pragma unroll
     for (int e = 0; e < V; ++e) acc[e] += t[e];
   }
-  for (int k = 0; k < n; ++k) {
-    unpack<T>(ld16(static_cast<const T*>(parts.p[k]) + off), t);
 #pragma unroll
-    for (int e = 0; e < V; ++e) acc[e] += t[e];
+  for (int k = 0; k < 16; ++k) {
+    if (k < n) {
+      unpack<T>(raw[k], t);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += t[e];
+    }
   }
   st16(out + off, pack<T>(acc));
 }

@@ -91,3 +91,14 @@ def test_recompute_backward_matches_stash(cfg):
     ra, rb = a.results(), b.results()
     for k in ra:
         assert np.array_equal(ra[k], rb[k], equal_nan=True), k
+
+
+@pytest.mark.parametrize("split", ["0", "1"])
+@pytest.mark.parametrize("cfg", [SMALL[1], SMALL[2], SMALL[3]], ids=lambda c: c.name)
+def test_attention_wave_forms(cfg, split, monkeypatch):
+    """Both attention kernel forms on every head size: four waves per 128
+    rows, and eight waves with the looped tiles dealt over two wave groups
+    (chosen automatically when the grid is small; forced here)."""
+    monkeypatch.setenv("TPL_ATTN_SPLIT", split)
+    report, st = check_case(cfg)
+    _assert_ok(report)
