@@ -84,6 +84,21 @@ def traced_kernels(st, steps, B, dtype):
     return agg
 
 
+def standin_sum_ms(st, passes, B):
+    """Event-timed milliseconds per layer pass (forward + backward) spent in
+    the all-reduce stand-in (shard_partial_sum), which on t GPUs would be an
+    RCCL all-reduce over xGMI rather than work of this rank."""
+    import torch
+    B.tpl_trace_enable(4096)
+    for _ in range(passes):
+        st.forward()
+        st.backward()
+    torch.cuda.synchronize()
+    recs = B.tpl_trace_read(4096)
+    B.tpl_trace_enable(0)
+    return sum(ms for name, ms, _ in recs if name == "partial_sum") / passes
+
+
 def roofline(agg, dtype):
     if not agg:   # no traced steps (--trace-steps 0)
         return None
@@ -376,6 +391,7 @@ def main():
     ms = time_loop(st.step, args.steps, torch)
     ms_layer = (time_loop(lambda: (st.forward(), st.backward()), max(3, args.steps // 2), torch)
                 if args.layer_only else None)
+    sums_ms = standin_sum_ms(st, 3, B) if args.layer_only else None
     agg = traced_kernels(st, args.trace_steps, B, cfg.dtype)
     loss = float(st.shared["loss"][0].item())
     emb = embedding_bench(cfg, args.steps, torch, B)
@@ -408,7 +424,13 @@ def main():
         "flops_per_step": fl,
         "layer_only": None if ms_layer is None else {
             "ms": round(ms_layer, 4), "tflops": round(fl["layer"] / (ms_layer / 1e3) / 1e12, 2),
-            "note": "layer fwd+bwd with its 4 all-reduce stand-ins, loss excluded"},
+            "note": "layer fwd+bwd with its 4 all-reduce stand-ins, loss excluded",
+            "excl_standin_sums": {
+                "ms": round(ms_layer - sums_ms, 4),
+                "tflops": round(fl["layer"] / ((ms_layer - sums_ms) / 1e3) / 1e12, 2),
+                "pct_of_mfma_peak": round(100 * fl["layer"] / ((ms_layer - sums_ms) / 1e3) / 1e12 / peak, 2),
+                "note": "the rank's own calls: layer time minus the event-timed shard_partial_sum launches "
+                        "(stand-ins for the all-reduce on t GPUs)"}},
         "loss": round(loss, 6),
         "roofline": roofline(agg, cfg.dtype),
         "embedding": emb,

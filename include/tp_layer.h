@@ -123,7 +123,7 @@ size_t tp_layer_saved_bytes(const tpl_desc* desc, tpl_block block);
  * partial: [N][h] out, this rank's row-parallel partial sum, without the
  *          row-parallel bias or the residual (summed by shard_partial_sum).
  * saved: tp_layer_saved_bytes() bytes (required: it also holds the block's
- *        intermediates -- LN output, qkv / u, attention output / GeLU output,
+ *        intermediates -- LN output, qkv / GeLU'(u), attention output / GeLU output,
  *        LN and softmax statistics -- and the backward's scratch). */
 tpl_status tp_layer_shard_fwd(const tpl_desc* desc, tpl_block block, const void* x,
                               const tpl_block_params* params, void* partial, void* saved,
@@ -154,7 +154,7 @@ tpl_status shard_partial_sum(const tpl_desc* desc, const void* const* partials, 
  *   TPL_BWD_SHARD_RECOMPUTE: activation recomputation (overview page section
  *     3: checkpointing trades compute for memory). As TPL_BWD_SHARD, but the
  *     block's forward stash (LN output and statistics; ATTN: qkv, ctx, LSE;
- *     MLP: u and GeLU(u)) is first recomputed from the block input x into
+ *     MLP: GeLU'(u) and GeLU(u)) is first recomputed from the block input x into
  *     `saved`, so `saved` need not hold this block's forward: one buffer of
  *     tp_layer_saved_bytes can serve every layer of a model. Results are
  *     identical to TPL_BWD_SHARD. A later TPL_BWD_REPLICATED call with the

@@ -72,9 +72,9 @@ tpl_status from_hip(hipError_t e) { return e == hipSuccess ? TPL_OK : TPL_ERR_HI
 // Regions are 256-byte aligned. ATTN: mu, rstd [N] f32; y [N][h]; qkv [N][3hr];
 // ctx [N][hr]; lse [b][a_r][s] f32; then backward scratch: dctx [N][hr],
 // dqkv [N][3hr], delta [b][a_r][s] f32, ws (column partials, f32).
-// MLP: mu, rstd; z [N][h]; u [N][fr]; act [N][fr]; then du [N][fr], ws.
+// MLP: mu, rstd; z [N][h]; GeLU'(u) [N][fr]; act [N][fr]; then du [N][fr], ws.
 enum { S_MU, S_RSTD, S_Y, S_QKV, S_CTX, S_LSE, S_DCTX, S_DQKV, S_DELTA, S_WS, S_COUNT };
-enum { S_Z = S_Y, S_U = S_QKV, S_ACT = S_CTX, S_DU = S_DCTX };
+enum { S_Z = S_Y, S_GP = S_QKV, S_ACT = S_CTX, S_DU = S_DCTX };
 
 struct Saved {
   size_t off[S_COUNT];
@@ -101,7 +101,7 @@ Saved saved_layout(const Dims& m, tpl_block block) {
     ws = std::max(ws, gemm_ws_floats(m.dt, m.h, m.hr, m.N));       // dW_o
     ws = std::max(ws, gemm_ws_floats(m.dt, 3 * m.hr, m.h, m.N));   // dW_qkv
   } else {
-    sz[S_U] = m.N * m.fr * es;
+    sz[S_GP] = m.N * m.fr * es;
     sz[S_ACT] = m.N * m.fr * es;
     sz[S_DU] = m.N * m.fr * es;
     ws = std::max(ws, colsum_ws_floats(m.N, m.fr));
@@ -234,7 +234,7 @@ size_t tp_layer_saved_bytes(const tpl_desc* desc, tpl_block block) {
 namespace {
 // The block's forward up to (not including) the row-parallel product: LN into
 // `saved`, then ATTN: qkv = y W_qkv^T + b, attention -> ctx, LSE; MLP: u = z
-// W_1^T + b, act = GeLU(u). Used by the forward and by the recomputing
+// W_1^T + b, kept as GeLU'(u), and act = GeLU(u). Used by the forward and by the recomputing
 // backward.
 tpl_status fwd_stash(const Dims& m, const tpl_desc* desc, tpl_block block, const void* x, const tpl_block_params* p,
                      void* saved, const Saved& L, hipStream_t s) {
@@ -256,9 +256,9 @@ tpl_status fwd_stash(const Dims& m, const tpl_desc* desc, tpl_block block, const
     a.lse = slot<float>(saved, L, S_LSE);
     TPL_TRY(launch_attn_fwd(a, s));
   } else {
-    void* u = slot<char>(saved, L, S_U);
+    void* gp = slot<char>(saved, L, S_GP);   // GeLU'(u), all the backward needs of u
     void* act = slot<char>(saved, L, S_ACT);
-    GemmDesc g = gemm(m, true, true, m.N, m.fr, m.h, y, m.h, p->w_in, m.h, u, m.fr);
+    GemmDesc g = gemm(m, true, true, m.N, m.fr, m.h, y, m.h, p->w_in, m.h, gp, m.fr);
     g.epi = EPI_BIAS_GELU;
     g.bias = p->b_in;
     g.C2 = act;
@@ -368,14 +368,14 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     TPL_TRY(launch_colsum(m.dt, dqkv, 3 * m.hr, m.N, 3 * m.hr, gr->d_b_in, ws, s));
     TPL_TRY(launch_gemm(gemm(m, true, false, m.N, m.h, 3 * m.hr, dqkv, 3 * m.hr, p->w_in, m.h, d_ln_partial, m.h), s));
   } else {
-    void* u = slot<char>(saved, L, S_U);
+    void* gp = slot<char>(saved, L, S_GP);
     void* act = slot<char>(saved, L, S_ACT);
     void* du = slot<char>(saved, L, S_DU);
-    // du = (dy W_2) * GeLU'(u); db_1 = colsum(du) from the product's column
+    // du = (dy W_2) * GeLU'(u) (stored by the forward); db_1 = colsum(du) from the product's column
     // partials when it provides them (bf16), else a separate pass below
     GemmDesc g = gemm(m, true, false, m.N, m.fr, m.h, dy, m.h, p->w_out, m.fr, du, m.fr);
     g.epi = EPI_DGELU;
-    g.C2 = u;
+    g.C2 = gp;
     g.ldc2 = m.fr;
     const int64_t cp = gemm_colpart_chunks(m.dt, m.N, m.fr);
     if (cp > 0) g.colpart = ws;

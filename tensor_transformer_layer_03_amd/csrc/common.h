@@ -135,14 +135,13 @@ __device__ __forceinline__ float normal_cdf_tail(float u, float& gauss) {
   const float half_erfc = 0.5f * poly * gauss;
   return u >= 0.0f ? 1.0f - half_erfc : half_erfc;                 // Phi(u)
 }
-__device__ __forceinline__ float gelu_f(float x) {
-  float g;
-  return x * normal_cdf_tail(x, g);
-}
-__device__ __forceinline__ float gelu_grad_f(float x) {
+// GeLU(u) and GeLU'(u) from one evaluation of Phi and phi (the forward
+// stores both: GeLU'(u) is what the backward needs of u).
+__device__ __forceinline__ void gelu_and_grad(float x, float& gelu, float& grad) {
   float g;
   const float cdf = normal_cdf_tail(x, g);
-  return fmaf(x * 0.39894228040143268f, g, cdf);
+  gelu = x * cdf;
+  grad = fmaf(x * 0.39894228040143268f, g, cdf);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

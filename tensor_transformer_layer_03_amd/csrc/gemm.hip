@@ -259,15 +259,20 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave) void gemm_kernel(Args g)
         }
         TC* cp = reinterpret_cast<TC*>(g.C) + (int64_t)m * g.ldc + n;
         if constexpr (EPI == EPI_DGELU) {
-          float u[4];
-          load4(reinterpret_cast<const T*>(g.C2) + (int64_t)m * g.ldc2 + n, u);
+          float gp[4];
+          load4(reinterpret_cast<const T*>(g.C2) + (int64_t)m * g.ldc2 + n, gp);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
+          for (int e = 0; e < 4; ++e) v[e] *= gp[e];
         }
-        store4(cp, v[0], v[1], v[2], v[3]);
         if constexpr (EPI == EPI_BIAS_GELU) {
+          float ge[4], gp[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gelu_and_grad(v[e], ge[e], gp[e]);
+          store4(cp, gp[0], gp[1], gp[2], gp[3]);
           T* ap = reinterpret_cast<T*>(g.C2) + (int64_t)m * g.ldc2 + n;
-          store4(ap, gelu_f(v[0]), gelu_f(v[1]), gelu_f(v[2]), gelu_f(v[3]));
+          store4(ap, ge[0], ge[1], ge[2], ge[3]);
+        } else {
+          store4(cp, v[0], v[1], v[2], v[3]);
         }
       }
     }
@@ -728,7 +733,9 @@ __device__ __forceinline__ void gemm_bf16_body(Args g) {
   constexpr int kCap = 2 * kStage / Stage::kRowBytes;   // rows the LDS holds
   constexpr int kRP = kCap >= BM ? BM : (kCap >= 128 ? 128 : (kCap >= 64 ? 64 : 32));
   static_assert(kRP >= WTM && BM % kRP == 0 && kRP % WTM == 0, "staging rows must hold whole wave tiles");
-  constexpr int kRounds = EPI == EPI_BIAS_GELU ? 2 : 1;   // u, then GeLU(u)
+  // GeLU epilogue: round 0 stages GeLU'(u) and leaves GeLU(u) in the
+  // accumulators, round 1 stages those
+  constexpr int kRounds = EPI == EPI_BIAS_GELU ? 2 : 1;
   BiasCols<TN> bias;
   if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias.load(g.bias, g.N, n0 + wn * WTN, lane);
   __syncthreads();
@@ -750,17 +757,23 @@ __device__ __forceinline__ void gemm_bf16_body(Args g) {
             for (int q = 0; q < 4; ++q) {
               const int nt = wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
               float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-              if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias.add(v, j, q);
+              if constexpr (EPI == EPI_BIAS) bias.add(v, j, q);
               if constexpr (EPI == EPI_DGELU) {
-                float u[4];
-                Stage::get4(smem, rt - p * kRP, nt, u);
+                float gp[4];
+                Stage::get4(smem, rt - p * kRP, nt, gp);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(u[e]);
+                for (int e = 0; e < 4; ++e) v[e] *= gp[e];
               }
               if constexpr (EPI == EPI_BIAS_GELU) {
-                if (round == 1) {
+                if (round == 0) {
+                  bias.add(v, j, q);
 #pragma unroll
-                  for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
+                  for (int e = 0; e < 4; ++e) {
+                    float ge, gp;
+                    gelu_and_grad(v[e], ge, gp);
+                    acc[i][j][4 * q + e] = ge;
+                    v[e] = gp;
+                  }
                 }
               }
               Stage::put4(smem, rt - p * kRP, nt, v);
@@ -1078,7 +1091,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
   // fragment read)
   using Stage = CStage<TC, BN, NW * 64>;
   static_assert(NS * kStage >= BM * Stage::kRowBytes, "the stages must hold the staged tile");
-  constexpr int kRounds = EPI == EPI_BIAS_GELU ? 2 : 1;   // u, then GeLU(u)
+  // GeLU epilogue: round 0 stages GeLU'(u) and leaves GeLU(u) in the
+  // accumulators, round 1 stages those
+  constexpr int kRounds = EPI == EPI_BIAS_GELU ? 2 : 1;
   BiasCols<TN> bias;
   if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias.load(g.bias, g.N, n0 + wn * WTN, lane);
   __syncthreads();
@@ -1093,11 +1108,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
         for (int q = 0; q < 4; ++q) {
           const int nt = wn * WTN + j * 32 + 8 * q + 4 * (lane >> 5);
           float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias.add(v, j, q);
+          if constexpr (EPI == EPI_BIAS) bias.add(v, j, q);
           if constexpr (EPI == EPI_BIAS_GELU) {
-            if (round == 1) {
+            if (round == 0) {
+              bias.add(v, j, q);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
+              for (int e = 0; e < 4; ++e) {
+                float ge, gp;
+                gelu_and_grad(v[e], ge, gp);
+                acc[i][j][4 * q + e] = ge;
+                v[e] = gp;
+              }
             }
           }
           Stage::put4(smem, rt, nt, v);

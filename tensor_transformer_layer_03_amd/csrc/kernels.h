@@ -29,8 +29,8 @@ struct TraceScope {
 enum Epilogue {
   EPI_NONE = 0,       // C = acc
   EPI_BIAS = 1,       // C = acc + bias[n]
-  EPI_BIAS_GELU = 2,  // C = u = acc + bias[n]; C2 = GeLU(u)
-  EPI_DGELU = 3,      // C = acc * GeLU'(C2[m][n])  (C2 holds u, read-only)
+  EPI_BIAS_GELU = 2,  // u = acc + bias[n]; C = GeLU'(u); C2 = GeLU(u)
+  EPI_DGELU = 3,      // C = acc * C2[m][n]  (C2 holds GeLU'(u) from EPI_BIAS_GELU, read-only)
   EPI_XENT = 4        // C = acc (logits); per-row (max, sum exp) of each tile column
 };
 struct GemmDesc {
