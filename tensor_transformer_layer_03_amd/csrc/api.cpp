@@ -100,6 +100,7 @@ Saved saved_layout(const Dims& m, tpl_block block) {
     ws = std::max(ws, colsum_ws_floats(m.N, 3 * m.hr));
     ws = std::max(ws, gemm_ws_floats(m.dt, m.h, m.hr, m.N));       // dW_o
     ws = std::max(ws, gemm_ws_floats(m.dt, 3 * m.hr, m.h, m.N));   // dW_qkv
+    ws = std::max(ws, gemm_dgrad_ws_floats(m.dt, m.N, m.hr, m.h));  // dctx split over K
   } else {
     sz[S_GP] = m.N * m.fr * es;
     sz[S_ACT] = m.N * m.fr * es;
@@ -347,8 +348,12 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     void* ctx = slot<char>(saved, L, S_CTX);
     void* dctx = slot<char>(saved, L, S_DCTX);
     void* dqkv = slot<char>(saved, L, S_DQKV);
-    // dctx = dy W_o ; dW_o = dy^T ctx
-    TPL_TRY(launch_gemm(gemm(m, true, false, m.N, m.hr, m.h, dy, m.h, p->w_out, m.hr, dctx, m.hr), s));
+    // dctx = dy W_o (split over K through the workspace when its grid is
+    // small: nothing else lives there yet) ; dW_o = dy^T ctx
+    GemmDesc gd = gemm(m, true, false, m.N, m.hr, m.h, dy, m.h, p->w_out, m.hr, dctx, m.hr);
+    gd.ws = ws;
+    gd.ws_floats = (L.total - L.off[S_WS]) / 4;   // the workspace is the last slot
+    TPL_TRY(launch_gemm(gd, s));
     GemmDesc gw = gemm(m, false, false, m.h, m.hr, m.N, dy, m.h, ctx, m.hr, gr->d_w_out, m.hr);
     gw.c_f32 = true;
     gw.ws = ws;

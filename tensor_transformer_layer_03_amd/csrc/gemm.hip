@@ -1175,12 +1175,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(TC* C, int64_t ldc, 
 // 256x256 grid is small and whose K is long (the loss's dH over the
 // vocabulary): every split writes fp32 partials into the workspace, summed
 // and rounded once afterwards. Bounded by the workspace capacity.
+int device_cus();
+
 SplitK splitk_dgrad_for(int dtype, int64_t M, int64_t N, int64_t K, size_t ws_floats) {
   SplitK r{1, (int)K, 0};
   if (dtype != DT_BF16 || getenv("TPL_GEMM_TILE") || M * N <= 0) return r;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles >= 384 || K < 8192) return r;
+  // about two rounds of splits at least 4096 deep; when K is too short for
+  // that to fill even one round (the output projection of a wide rank:
+  // 48 tiles, K = 12288), one round of splits at least 2048 deep instead
+  const int64_t cus = device_cus();
   int64_t sp = std::min<int64_t>((512 + tiles - 1) / tiles, K / 4096);
+  if (tiles * sp < cus) sp = std::min<int64_t>(cus / tiles, K / 2048);
   sp = std::min<int64_t>(sp, (int64_t)(ws_floats / (size_t)(M * N)));
   if (sp < 2) return r;
   const int64_t chunk = ((K + sp - 1) / sp + 63) / 64 * 64;
@@ -1539,6 +1546,11 @@ int xent_gemm_tile_cols(int dtype, int64_t M, int64_t N) {
   if (dtype != DT_BF16 || M <= 0 || N <= 0) return 0;
   if (((M + 255) / 256) * ((N + 255) / 256) >= 384) return (int)((N + 255) / 256);
   return (int)((N + 127) / 128);
+}
+size_t gemm_dgrad_ws_floats(int dtype, int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0) return 0;
+  const SplitK sk = splitk_dgrad_for(dtype, M, N, K, ~size_t(0));
+  return sk.splits > 1 ? (size_t)sk.splits * (size_t)M * (size_t)N : 0;
 }
 size_t gemm_ws_floats(int dtype, int64_t M, int64_t N, int64_t K) {
   const SplitK sk = splitk_for(dtype, M, N, K);

@@ -61,6 +61,9 @@ hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
 // Floats of split-K workspace the product (M, N, K) with both operands MN-major
 // and an fp32 output takes (0: it is not split).
 size_t gemm_ws_floats(int dtype, int64_t M, int64_t N, int64_t K);
+// Workspace floats a bf16 activation-gradient product (A K-major, B MN-major,
+// M x N output, depth K) uses when it splits over K (0 when it does not).
+size_t gemm_dgrad_ws_floats(int dtype, int64_t M, int64_t N, int64_t K);
 // Row blocks of the column partials an EPI_DGELU product writes to colpart.
 int64_t gemm_colpart_chunks(int dtype, int64_t M, int64_t N);
 // Number of tile columns of the logits product with the fused statistics
