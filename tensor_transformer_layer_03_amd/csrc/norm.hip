@@ -94,6 +94,130 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(const T* __restrict__ x, co
   if (lane == 0) { mu_out[row] = mean; rstd_out[row] = rstd; }
 }
 
+// ------------------------------------------------------------------ wide rows
+// Rows wider than two 16-B chunks per lane (hidden > 1024 in bf16): one
+// workgroup of four waves per row, thread t caching chunks t + 256 i (PER per
+// thread), so a row streams with 4x the loads in flight and the register
+// cache stays small. Row sums: each wave's sum, then the four added in wave
+// order through LDS (deterministic).
+__device__ __forceinline__ float block4_sum(float v, float* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <typename T, int PER>
+__global__ __launch_bounds__(256) void ln_fwd_wide_kernel(const T* __restrict__ x, const T* __restrict__ g,
+                                                          const T* __restrict__ bta, T* __restrict__ y,
+                                                          float* __restrict__ mu_out, float* __restrict__ rstd_out,
+                                                          int cols, float eps) {
+  constexpr int V = Vec16<T>::N;
+  __shared__ float red[2][4];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int nch = cols / V;
+  const T* xr = x + row * cols;
+  u32x4 cache[PER];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int ch = tid + 256 * i;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (ch < nch) raw = ld16(xr + ch * V);
+    cache[i] = raw;
+    float v[V];
+    unpack<T>(raw, v);
+#pragma unroll
+    for (int e = 0; e < V; ++e) sum += v[e];
+  }
+  const float mean = block4_sum(sum, red[0]) / cols;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (tid + 256 * i < nch) {
+      float v[V];
+      unpack<T>(cache[i], v);
+#pragma unroll
+      for (int e = 0; e < V; ++e) { const float d = v[e] - mean; sq += d * d; }
+    }
+  }
+  const float rstd = rsqrtf(block4_sum(sq, red[1]) / cols + eps);
+  T* yr = y + row * cols;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int ch = tid + 256 * i;
+    if (ch < nch) {
+      float v[V], gv[V], bv[V];
+      unpack<T>(cache[i], v);
+      unpack<T>(ld16(g + ch * V), gv);
+      unpack<T>(ld16(bta + ch * V), bv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) v[e] = (v[e] - mean) * rstd * gv[e] + bv[e];
+      st16(yr + ch * V, pack<T>(v));
+    }
+  }
+  if (tid == 0) { mu_out[row] = mean; rstd_out[row] = rstd; }
+}
+
+// dx = dy + rstd * (gd - mean(gd) - xhat * mean(gd * xhat)),  gd = dsum * gamma
+// (as ln_bwd_kernel below), one workgroup per row.
+template <typename T, int PER>
+__global__ __launch_bounds__(256) void ln_bwd_wide_kernel(const T* __restrict__ dy, const T* __restrict__ dsum,
+                                                          const T* __restrict__ x, const float* __restrict__ mu,
+                                                          const float* __restrict__ rstd, const T* __restrict__ g,
+                                                          T* __restrict__ dx, int cols) {
+  constexpr int V = Vec16<T>::N;
+  __shared__ float red[2][4];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int nch = cols / V;
+  const float m = mu[row], rs = rstd[row];
+  u32x4 cd[PER], cx[PER], cy[PER];
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int ch = tid + 256 * i;
+    u32x4 rd = {0u, 0u, 0u, 0u}, rx = rd, ry = rd;
+    if (ch < nch) {
+      rd = ld16(dsum + row * cols + ch * V);
+      rx = ld16(x + row * cols + ch * V);
+      ry = ld16(dy + row * cols + ch * V);
+      float dv[V], xv[V], gv[V];
+      unpack<T>(rd, dv);
+      unpack<T>(rx, xv);
+      unpack<T>(ld16(g + ch * V), gv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float gd = dv[e] * gv[e];
+        s1 += gd;
+        s2 += gd * (xv[e] - m) * rs;
+      }
+    }
+    cd[i] = rd;
+    cx[i] = rx;
+    cy[i] = ry;
+  }
+  const float mean1 = block4_sum(s1, red[0]) / cols, mean2 = block4_sum(s2, red[1]) / cols;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int ch = tid + 256 * i;
+    if (ch < nch) {
+      float dv[V], xv[V], gv[V], yv[V];
+      unpack<T>(cd[i], dv);
+      unpack<T>(cx[i], xv);
+      unpack<T>(ld16(g + ch * V), gv);
+      unpack<T>(cy[i], yv);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float xh = (xv[e] - m) * rs;
+        yv[e] += rs * (dv[e] * gv[e] - mean1 - xh * mean2);
+      }
+      st16(dx + row * cols + ch * V, pack<T>(yv));
+    }
+  }
+}
+
 // ------------------------------------------------------------------ LayerNorm backward (rows)
 // dx = dy + rstd * (gd - mean(gd) - xhat * mean(gd * xhat)),  gd = dsum * gamma.
 template <typename T, int MAXC>
@@ -443,19 +567,53 @@ int maxc_for(int dtype, int cols) {
   return -1;
 }
 
+// wave-per-row kernels: at most two chunks per lane (wider rows take the
+// one-workgroup-per-row kernels)
 #define TPL_MAXC_SWITCH(M, CALL)      \
   switch (M) {                        \
     case 1: { constexpr int MC = 1; return CALL; }  \
     case 2: { constexpr int MC = 2; return CALL; }  \
-    case 4: { constexpr int MC = 4; return CALL; }  \
-    case 8: { constexpr int MC = 8; return CALL; }  \
-    case 16: { constexpr int MC = 16; return CALL; } \
-    case 24: { constexpr int MC = 24; return CALL; } \
-    case 32: { constexpr int MC = 32; return CALL; } \
   }                                   \
   return hipErrorInvalidValue;
 
 int64_t n_chunks(int64_t rows) { return (rows + kRowsPerChunk - 1) / kRowsPerChunk; }
+
+// Chunks per thread of the one-workgroup-per-row kernels (256 threads), or -1.
+int wide_per(int dtype, int cols) {
+  const int v = dtype == DT_BF16 ? 8 : 4;
+  const int need = (cols / v + 255) / 256;
+  const int sizes[] = {1, 2, 4, 8};
+  for (int m : sizes)
+    if (need <= m) return m;
+  return -1;
+}
+
+#define TPL_PER_SWITCH(P, CALL)       \
+  switch (P) {                        \
+    case 1: { constexpr int PC = 1; return CALL; }  \
+    case 2: { constexpr int PC = 2; return CALL; }  \
+    case 4: { constexpr int PC = 4; return CALL; }  \
+    case 8: { constexpr int PC = 8; return CALL; }  \
+  }                                   \
+  return hipErrorInvalidValue;
+
+template <typename T, int PER>
+hipError_t ln_fwd_wide_t(const void* x, const void* g, const void* b, void* y, float* mu, float* rstd, int64_t rows,
+                         int cols, float eps, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL((ln_fwd_wide_kernel<T, PER>), dim3((unsigned)rows), dim3(256), 0, s, static_cast<const T*>(x),
+                     static_cast<const T*>(g), static_cast<const T*>(b), static_cast<T*>(y), mu, rstd, cols, eps);
+  return hipGetLastError();
+}
+template <typename T, int PER>
+hipError_t ln_bwd_wide_t(const void* dy, const void* dsum, const void* x, const float* mu, const float* rstd,
+                         const void* g, void* dx, int64_t rows, int cols, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL((ln_bwd_wide_kernel<T, PER>), dim3((unsigned)rows), dim3(256), 0, s, static_cast<const T*>(dy),
+                     static_cast<const T*>(dsum), static_cast<const T*>(x), mu, rstd, static_cast<const T*>(g),
+                     static_cast<T*>(dx), cols);
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -466,6 +624,11 @@ hipError_t launch_layernorm_fwd(int dtype, const void* x, const void* g, const v
                                 float* rstd, int64_t rows, int cols, float eps, hipStream_t s) {
   TraceScope trace(K_LN_FWD, s, (double)rows * cols * 2 * dtype_size(dtype) + rows * 8.0);
   const int mc = maxc_for(dtype, cols);
+  if (mc > 2) {   // wide rows: one four-wave workgroup per row
+    const int per = wide_per(dtype, cols);
+    if (dtype == DT_BF16) { TPL_PER_SWITCH(per, (ln_fwd_wide_t<bf16, PC>(x, g, b, y, mu, rstd, rows, cols, eps, s))) }
+    TPL_PER_SWITCH(per, (ln_fwd_wide_t<float, PC>(x, g, b, y, mu, rstd, rows, cols, eps, s)))
+  }
   if (dtype == DT_BF16) { TPL_MAXC_SWITCH(mc, (ln_fwd_t<bf16, MC>(x, g, b, y, mu, rstd, rows, cols, eps, s))) }
   TPL_MAXC_SWITCH(mc, (ln_fwd_t<float, MC>(x, g, b, y, mu, rstd, rows, cols, eps, s)))
 }
@@ -474,6 +637,11 @@ static hipError_t ln_bwd_rows(int dtype, const void* dy, const void* dsum, const
                               const float* rstd, const void* g, void* dx, int64_t rows, int cols, hipStream_t s) {
   TraceScope trace(K_LN_BWD, s, (double)rows * cols * 4 * dtype_size(dtype) + rows * 8.0);
   const int mc = maxc_for(dtype, cols);
+  if (mc > 2) {   // wide rows: one four-wave workgroup per row
+    const int per = wide_per(dtype, cols);
+    if (dtype == DT_BF16) { TPL_PER_SWITCH(per, (ln_bwd_wide_t<bf16, PC>(dy, dsum, x, mu, rstd, g, dx, rows, cols, s))) }
+    TPL_PER_SWITCH(per, (ln_bwd_wide_t<float, PC>(dy, dsum, x, mu, rstd, g, dx, rows, cols, s)))
+  }
   if (dtype == DT_BF16) { TPL_MAXC_SWITCH(mc, (ln_bwd_t<bf16, MC>(dy, dsum, x, mu, rstd, g, dx, rows, cols, s))) }
   TPL_MAXC_SWITCH(mc, (ln_bwd_t<float, MC>(dy, dsum, x, mu, rstd, g, dx, rows, cols, s)))
 }

@@ -102,3 +102,22 @@ def test_attention_wave_forms(cfg, split, monkeypatch):
     monkeypatch.setenv("TPL_ATTN_SPLIT", split)
     report, st = check_case(cfg)
     _assert_ok(report)
+
+
+WIDE = [
+    synth.tiny_config("f32", hidden=768, heads=12, head_dim=64, ffn=1536, tp=2, seq=40, micro_batch=2,
+                      vocab=128, causal=True, sigma_w=0.05, index=56, name="small_f32_wide_rows"),
+    # weights at the workloads' scale: with N(0, 0.05) at this width the logits have std ~3 and the
+    # bf16-rounded logits alone put the loss gradient ~1.5% off the float64 oracle
+    synth.tiny_config("bf16", hidden=1280, heads=10, head_dim=128, ffn=2560, tp=2, seq=33, micro_batch=2,
+                      vocab=256, causal=False, sigma_w=0.02, index=57, name="small_bf16_wide_rows"),
+]
+
+
+@pytest.mark.parametrize("cfg", WIDE, ids=lambda c: c.name)
+def test_wide_rows(cfg):
+    """Hidden sizes past two 16-B chunks per lane (fp32 > 512, bf16 > 1024):
+    LayerNorm forward and backward rows run one four-wave workgroup per row,
+    here with a row that leaves part of the workgroup's threads idle."""
+    report, st = check_case(cfg)
+    _assert_ok(report)
