@@ -937,11 +937,15 @@ __global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL =
   }
 }
 
-// SPL = 2: eight waves, the second four taking every other query tile; the
-// two partial dK and dV are added at the end (even parity first).
-template <int D, bool CAUSAL, int SPL>
-__global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL == 2 ? 2 : (D == 64 ? 2 : 1)))) void attn_bwd_dkdv_bf16_kernel(Args a) {
-  constexpr int NT = 256 * SPL, BKB = 128, BQ = 64;
+// KW waves of 32 keys each per workgroup (BKB = 32 KW keys). SPL = 2: a
+// second group of KW waves takes every other query tile; the two partial dK
+// and dV are added at the end (even parity first). Forms: (KW 4, SPL 1) by
+// default; (4, 2) for small grids at head size 64; (2, 2) for small grids at
+// 96 and 128, where two waves per SIMD would not fit the registers: twice the
+// workgroups of half the keys, one wave per SIMD.
+template <int D, bool CAUSAL, int SPL, int KW>
+__global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(KW * SPL == 8 ? 2 : (D == 64 ? 2 : 1)))) void attn_bwd_dkdv_bf16_kernel(Args a) {
+  constexpr int NT = 64 * KW * SPL, BKB = 32 * KW, BQ = 64;
   using Tile = NatTile<D, NT>;
   __shared__ __attribute__((aligned(16))) char sQ[2][SPL][Tile::kBytes];
   __shared__ __attribute__((aligned(16))) char sdO[2][SPL][Tile::kBytes];
@@ -950,7 +954,7 @@ __global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL =
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, grp = lane >> 5;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
-  const int wave = wid & 3, par = wid >> 2;                     // key sub-tile, query-tile parity
+  const int wave = wid % KW, par = wid / KW;                    // key sub-tile, query-tile parity
   // 1-D grid dealt heaviest key tiles (the first ones, under a causal mask) first over all heads
   const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs, kb = blockIdx.x / bhs;
   const int b = bh / a.heads, hd = bh % a.heads;
@@ -1085,7 +1089,8 @@ __global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL =
   if constexpr (SPL == 2) {
     // odd-parity partial dK (through the free Q stages) and dV (through the
     // dO stages): element e of lane i at [e][i]
-    static_assert(D / 2 * 256 * 4 <= (int)sizeof(sQ), "the Q stages must hold the exchanged dK");
+    constexpr int kLanes = 64 * KW;   // lanes of one parity group
+    static_assert(D / 2 * kLanes * 4 <= (int)sizeof(sQ), "the Q stages must hold the exchanged dK");
     float* xk = reinterpret_cast<float*>(&sQ[0][0][0]);
     float* xv = reinterpret_cast<float*>(&sdO[0][0][0]);
     const int slot = wave * 64 + lane;
@@ -1094,8 +1099,8 @@ __global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL =
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          xk[(dt * 16 + r) * 256 + slot] = dk[dt][r];
-          xv[(dt * 16 + r) * 256 + slot] = dv[dt][r];
+          xk[(dt * 16 + r) * kLanes + slot] = dk[dt][r];
+          xv[(dt * 16 + r) * kLanes + slot] = dv[dt][r];
         }
     }
     __syncthreads();
@@ -1104,8 +1109,8 @@ __global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL =
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        dk[dt][r] += xk[(dt * 16 + r) * 256 + slot];
-        dv[dt][r] += xv[(dt * 16 + r) * 256 + slot];
+        dk[dt][r] += xk[(dt * 16 + r) * kLanes + slot];
+        dv[dt][r] += xv[(dt * 16 + r) * kLanes + slot];
       }
   }
   if (my_k < s) {
@@ -1177,15 +1182,17 @@ hipError_t bwd_t(const AttnDesc& d, hipStream_t s) {
   {
     TraceScope trace(K_ATTN_BWD_DKDV, s, 6.0 * attn_pairs(d) * d.head_dim);   // dV, dP, dK
     if constexpr (sizeof(T) == 2) {
-      // eight waves only at head size 64: with 96 or 128 the dK, dV, K and V
-      // registers of two waves per SIMD exceed the register file (spills)
-      constexpr int kSpl = D == 64 ? 2 : 1;
-      if (kSpl == 2 && attn_split(d)) {
-        if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, kSpl>), grid, dim3(256 * kSpl), 0, s, a);
-        else hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false, kSpl>), grid, dim3(256 * kSpl), 0, s, a);
+      // small grids: eight waves per 128 keys at head size 64; at 96 and 128
+      // (where the dK, dV, K and V registers of two waves per SIMD would
+      // spill) four waves per 64 keys, so twice the workgroups
+      if (attn_split(d)) {
+        constexpr int kKw = D == 64 ? 4 : 2;
+        dim3 g2((unsigned)(((d.seq + 32 * kKw - 1) / (32 * kKw)) * d.batch * d.heads));
+        if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, 2, kKw>), g2, dim3(128 * kKw), 0, s, a);
+        else hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false, 2, kKw>), g2, dim3(128 * kKw), 0, s, a);
       } else {
-        if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, 1>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false, 1>), grid, dim3(256), 0, s, a);
+        if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, true, 1, 4>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D, false, 1, 4>), grid, dim3(256), 0, s, a);
       }
     } else {
       if (d.causal) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, true>), grid, dim3(256), 0, s, a);
