@@ -621,20 +621,24 @@ struct NatTile {
   }
 };
 
-// SPL = 2 (used when the grid has under two waves per SIMD): eight waves, the
-// second four taking every other key tile of the same 128 queries; their
-// partial (O, max, sum) are merged at the end through LDS in a fixed order.
-template <int D, bool CAUSAL, int SPL>
-__global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL == 2 ? 2 : (D == 64 ? 3 : 1)))) void attn_fwd_bf16_kernel(Args a) {
-  constexpr int NT = 256 * SPL, BQ = 128, BKV = 64;
+// KW waves of 32 queries each per workgroup (BQ = 32 KW). SPL = 2 (used
+// when the grid has under two waves per SIMD): a second group of KW waves
+// takes every other key tile of the same queries; their partial (O, max,
+// sum) are merged at the end through LDS in a fixed order. Forms: (KW 4,
+// SPL 1) by default, (4, 2) for small grids at head size 64 and 96, (2, 2)
+// at 128 (one wave per SIMD there: twice the workgroups of half the rows).
+template <int D, bool CAUSAL, int SPL, int KW>
+__global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(KW * SPL == 8 ? 2 : (D == 64 ? 3 : 1)))) void attn_fwd_bf16_kernel(Args a) {
+  constexpr int NT = 64 * KW * SPL, BQ = 32 * KW, BKV = 64;
+  constexpr int kLanes = 64 * KW;   // lanes of one parity group
   using Tile = NatTile<D, NT>;
   __shared__ __attribute__((aligned(16))) char sK[2][SPL][Tile::kBytes];
   __shared__ __attribute__((aligned(16))) char sV[2][SPL][Tile::kBytes];
-  __shared__ float sML[SPL == 2 ? 2 * 256 : 1];
+  __shared__ float sML[SPL == 2 ? 2 * kLanes : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, grp = lane >> 5;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
-  const int wave = wid & 3, par = wid >> 2;                     // query sub-tile, key-tile parity
+  const int wave = wid % KW, par = wid / KW;                    // query sub-tile, key-tile parity
   // 1-D grid dealt heaviest query tiles first over all heads (causal tiles
   // differ up to seq/BQ-fold in work, so the last to start are the short ones)
   const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs;
@@ -759,27 +763,27 @@ __global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL =
   if constexpr (SPL == 2) {
     // the odd-parity wave of each query sub-tile hands (O, max, sum) to its
     // partner through the free K stages: element e of lane i at [e][i]
-    static_assert(D / 2 * 256 * 4 <= (int)sizeof(sK), "the K stages must hold the exchanged O");
+    static_assert(D / 2 * kLanes * 4 <= (int)sizeof(sK), "the K stages must hold the exchanged O");
     float* xo = reinterpret_cast<float*>(&sK[0][0][0]);
     const int slot = wave * 64 + lane;
     if (par == 1) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xo[(dt * 16 + r) * 256 + slot] = o[dt][r];
+        for (int r = 0; r < 16; ++r) xo[(dt * 16 + r) * kLanes + slot] = o[dt][r];
       sML[slot] = m;
-      sML[256 + slot] = l;
+      sML[kLanes + slot] = l;
     }
     __syncthreads();
     if (par == 1) return;
-    const float m1 = sML[slot], l1 = sML[256 + slot];
+    const float m1 = sML[slot], l1 = sML[kLanes + slot];
     const float mn = fmaxf(m, m1);
     const float mc = mn == -INFINITY ? 0.f : mn * c;
     const float a0 = __builtin_amdgcn_exp2f(m * c - mc), a1 = __builtin_amdgcn_exp2f(m1 * c - mc);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] = o[dt][r] * a0 + xo[(dt * 16 + r) * 256 + slot] * a1;
+      for (int r = 0; r < 16; ++r) o[dt][r] = o[dt][r] * a0 + xo[(dt * 16 + r) * kLanes + slot] * a1;
     l = l * a0 + l1 * a1;
     m = mn;
   }
@@ -792,18 +796,20 @@ __global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL =
   }
 }
 
-// SPL = 2: eight waves, the second four taking every other key tile; the two
-// partial dQ are added at the end (even parity first).
-template <int D, bool CAUSAL, int SPL>
-__global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL == 2 ? 2 : (D == 64 ? 3 : 1)))) void attn_bwd_dq_bf16_kernel(Args a) {
-  constexpr int NT = 256 * SPL, BQ = 128, BKV = 64;
+// KW waves of 32 queries per workgroup; SPL = 2: a second group of KW waves
+// takes every other key tile; the two partial dQ are added at the end (even
+// parity first). Forms as for the forward.
+template <int D, bool CAUSAL, int SPL, int KW>
+__global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(KW * SPL == 8 ? 2 : (D == 64 ? 3 : 1)))) void attn_bwd_dq_bf16_kernel(Args a) {
+  constexpr int NT = 64 * KW * SPL, BQ = 32 * KW, BKV = 64;
+  constexpr int kLanes = 64 * KW;   // lanes of one parity group
   using Tile = NatTile<D, NT>;
   __shared__ __attribute__((aligned(16))) char sK[2][SPL][Tile::kBytes];
   __shared__ __attribute__((aligned(16))) char sV[2][SPL][Tile::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, grp = lane >> 5;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
-  const int wave = wid & 3, par = wid >> 2;                     // query sub-tile, key-tile parity
+  const int wave = wid % KW, par = wid / KW;                    // query sub-tile, key-tile parity
   // 1-D grid dealt heaviest query tiles first over all heads (causal tiles
   // differ up to seq/BQ-fold in work, so the last to start are the short ones)
   const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs;
@@ -915,21 +921,21 @@ __global__ __launch_bounds__(256 * SPL) __attribute__((amdgpu_waves_per_eu(SPL =
   }
   if constexpr (SPL == 2) {
     // odd-parity partial dQ through the free K stages: element e of lane i at [e][i]
-    static_assert(D / 2 * 256 * 4 <= (int)sizeof(sK), "the K stages must hold the exchanged dQ");
+    static_assert(D / 2 * kLanes * 4 <= (int)sizeof(sK), "the K stages must hold the exchanged dQ");
     float* xq = reinterpret_cast<float*>(&sK[0][0][0]);
     const int slot = wave * 64 + lane;
     if (par == 1) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xq[(dt * 16 + r) * 256 + slot] = dq[dt][r];
+        for (int r = 0; r < 16; ++r) xq[(dt * 16 + r) * kLanes + slot] = dq[dt][r];
     }
     __syncthreads();
     if (par == 1) return;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dq[dt][r] += xq[(dt * 16 + r) * 256 + slot];
+      for (int r = 0; r < 16; ++r) dq[dt][r] += xq[(dt * 16 + r) * kLanes + slot];
   }
   if (my_q < s) {
     bf16* dQg = reinterpret_cast<bf16*>(a.dqkv) + (int64_t)b * s * a.ld_qkv + hd * D;
@@ -1152,12 +1158,14 @@ hipError_t fwd_t(const AttnDesc& d, hipStream_t s) {
   Args a = make_args(d);
   dim3 grid((unsigned)(((d.seq + 127) / 128) * d.batch * d.heads));
   if constexpr (sizeof(T) == 2) {
-    if (attn_split(d)) {
-      if (d.causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, 2>), grid, dim3(512), 0, s, a);
-      else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, 2>), grid, dim3(512), 0, s, a);
+    if (attn_split(d)) {   // small grids: see attn_fwd_bf16_kernel (64 rows per workgroup measured
+      constexpr int kKw = D == 128 ? 2 : 4;   // faster at head size 128 only)
+      dim3 g2((unsigned)(((d.seq + 32 * kKw - 1) / (32 * kKw)) * d.batch * d.heads));
+      if (d.causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, 2, kKw>), g2, dim3(128 * kKw), 0, s, a);
+      else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, 2, kKw>), g2, dim3(128 * kKw), 0, s, a);
     } else {
-      if (d.causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, 1>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, 1>), grid, dim3(256), 0, s, a);
+      if (d.causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true, 1, 4>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false, 1, 4>), grid, dim3(256), 0, s, a);
     }
   } else {
     if (d.causal) hipLaunchKernelGGL((attn_fwd_kernel<T, D, true>), grid, dim3(256), 0, s, a);
@@ -1203,12 +1211,14 @@ hipError_t bwd_t(const AttnDesc& d, hipStream_t s) {
   }
   TraceScope trace(K_ATTN_BWD_DQ, s, 2.0 * attn_pairs(d) * d.head_dim);     // dQ
   if constexpr (sizeof(T) == 2) {
-    if (attn_split(d)) {
-      if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, 2>), grid, dim3(512), 0, s, a);
-      else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false, 2>), grid, dim3(512), 0, s, a);
+    if (attn_split(d)) {   // small grids: see attn_bwd_dq_bf16_kernel (64 rows per workgroup
+      constexpr int kKw = D == 128 ? 2 : 4;   // measured faster at head size 128 only)
+      dim3 g2((unsigned)(((d.seq + 32 * kKw - 1) / (32 * kKw)) * d.batch * d.heads));
+      if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, 2, kKw>), g2, dim3(128 * kKw), 0, s, a);
+      else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false, 2, kKw>), g2, dim3(128 * kKw), 0, s, a);
     } else {
-      if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, 1>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false, 1>), grid, dim3(256), 0, s, a);
+      if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, true, 1, 4>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D, false, 1, 4>), grid, dim3(256), 0, s, a);
     }
   } else {
     if (d.causal) hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, true>), grid, dim3(256), 0, s, a);

@@ -1181,15 +1181,27 @@ SplitK splitk_dgrad_for(int dtype, int64_t M, int64_t N, int64_t K, size_t ws_fl
   SplitK r{1, (int)K, 0};
   if (dtype != DT_BF16 || getenv("TPL_GEMM_TILE") || M * N <= 0) return r;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles >= 384 || K < 8192) return r;
-  // about two rounds of splits at least 4096 deep; when K is too short for
-  // that to fill even one round (the output projection of a wide rank:
-  // 48 tiles, K = 12288), one round of splits at least 2048 deep instead
+  if (tiles >= 384) return r;
   const int64_t cus = device_cus();
-  int64_t sp = std::min<int64_t>((512 + tiles - 1) / tiles, K / 4096);
-  if (tiles * sp < cus) sp = std::min<int64_t>(cus / tiles, K / 2048);
+  int64_t sp = 0;
+  if (K >= 8192) {
+    // 256x256 tiles: about two rounds of splits at least 4096 deep; when K is
+    // too short for that to fill even one round (the output projection of a
+    // wide rank: 48 tiles, K = 12288), one round of splits at least 2048 deep
+    sp = std::min<int64_t>((512 + tiles - 1) / tiles, K / 4096);
+    if (tiles * sp < cus) sp = std::min<int64_t>(cus / tiles, K / 2048);
+    r.tile = 256;
+  } else {
+    // 128x128 tiles (two workgroups per CU) filling under half their slots
+    // (the output projection of a narrow rank: 96 tiles, K = 3072): splits at
+    // least 1024 deep up to about one round
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    if (t128 * 2 >= 2 * cus || K < 2048) return r;
+    sp = std::min<int64_t>(2 * cus / t128, K / 1024);
+    r.tile = 128;
+  }
   sp = std::min<int64_t>(sp, (int64_t)(ws_floats / (size_t)(M * N)));
-  if (sp < 2) return r;
+  if (sp < 2) return SplitK{1, (int)K, 0};
   const int64_t chunk = ((K + sp - 1) / sp + 63) / 64 * 64;
   r.splits = (int)((K + chunk - 1) / chunk);
   r.kchunk = (int)chunk;
@@ -1432,8 +1444,8 @@ hipError_t run_tiles(const GemmDesc& d, hipStream_t s) {
   }
 }
 
-// bf16 dgrad split over K: the 256x256 8-wave kernel writes every split's
-// fp32 partial into the workspace (C = ws, splits s >= 1 at ws + s*M*N), then
+// bf16 dgrad split over K: the 256x256 8-wave (or 128x128 4-wave) kernel
+// writes every split's fp32 partial into the workspace (C = ws, splits s >= 1 at ws + s*M*N), then
 // one pass sums them in split order and rounds to bf16.
 hipError_t run_dgrad_split(const GemmDesc& d, const SplitK& sk, hipStream_t s) {
   Args a{};
@@ -1443,15 +1455,20 @@ hipError_t run_dgrad_split(const GemmDesc& d, const SplitK& sk, hipStream_t s) {
   a.C2 = nullptr; a.ldc2 = 0;
   a.bias = nullptr;
   a.M = (int)d.M; a.N = (int)d.N; a.K = (int)d.K;
-  a.tiles_m = (a.M + 255) / 256;
-  a.tiles_n = (a.N + 255) / 256;
+  const int bt = sk.tile == 128 ? 128 : 256;
+  a.tiles_m = (a.M + bt - 1) / bt;
+  a.tiles_n = (a.N + bt - 1) / bt;
   a.targets = nullptr; a.v0 = 0; a.xpart = nullptr;
   a.splits = sk.splits;
   a.kchunk = sk.kchunk;
   a.ws = d.ws + (int64_t)d.M * d.N;
   const int nblk = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, true, false, false, EPI_NONE, float>), dim3(nblk * a.splits),
-                     dim3(512), 0, s, a);
+  if (bt == 128)
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, true, false, false, EPI_NONE, float>),
+                       dim3(nblk * a.splits), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, true, false, false, EPI_NONE, float>),
+                       dim3(nblk * a.splits), dim3(512), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t quads = (d.M * d.N + 3) / 4;
