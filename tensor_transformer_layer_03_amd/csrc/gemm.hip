@@ -1557,12 +1557,17 @@ hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
 
 }  // namespace
 
-// The fused-statistics logits product uses the 256x256 four-stage tile when
-// that gives at least 384 workgroups, else its 128x128 form.
+// The fused-statistics logits product takes the 256x256 four-stage tile or
+// its 128x128 form (two workgroups per CU), by the forward products' cost
+// model: rounds over the CUs x tile area x workgroups per CU / throughput
+// (1.0 and 0.7), a partly filled round costing a whole one.
 int xent_gemm_tile_cols(int dtype, int64_t M, int64_t N) {
   if (dtype != DT_BF16 || M <= 0 || N <= 0) return 0;
-  if (((M + 255) / 256) * ((N + 255) / 256) >= 384) return (int)((N + 255) / 256);
-  return (int)((N + 127) / 128);
+  const int64_t cus = device_cus();
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256), t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  const double c256 = (double)((t256 + cus - 1) / cus) * 65536.0;
+  const double c128 = (double)((t128 + 2 * cus - 1) / (2 * cus)) * 32768.0 / 0.7;
+  return c256 <= c128 ? (int)((N + 255) / 256) : (int)((N + 127) / 128);
 }
 size_t gemm_dgrad_ws_floats(int dtype, int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0) return 0;

@@ -185,6 +185,68 @@ __global__ __launch_bounds__(1024) void xent_finish_kernel(StatPtrs st, int t, i
   }
 }
 
+// The same for t <= 8 ranks: each thread loads all ranks' (max, sum, target
+// logit) of its kB rows at once, so one round of load latency serves a batch
+// instead of 2t dependent rounds. Ranks past t read as (-inf, 0, 0): the max
+// is unchanged and the sums gain exact zeros after rank t-1, so the results
+// equal xent_finish_kernel's bit for bit.
+__global__ __launch_bounds__(1024) void xent_finish8_kernel(StatPtrs st, int t, int64_t rows,
+                                                            const uint8_t* __restrict__ mask,
+                                                            float* __restrict__ lse, float* __restrict__ loss_rows,
+                                                            float* __restrict__ loss) {
+  constexpr int kB = 2;
+  float acc = 0.f, cnt = 0.f;
+  for (int64_t r0 = threadIdx.x; r0 < rows; r0 += 1024 * kB) {
+    float mk[8][kB], sk[8][kB], tk[8][kB];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int64_t r = r0 + 1024 * u;
+        mk[k][u] = -INFINITY; sk[k][u] = 0.f; tk[k][u] = 0.f;
+        if (k < t && r < rows) {
+          mk[k][u] = st.p[k][r * 3];
+          sk[k][u] = st.p[k][r * 3 + 1];
+          tk[k][u] = st.p[k][r * 3 + 2];
+        }
+      }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int64_t r = r0 + 1024 * u;
+      if (r >= rows) continue;
+      float M = -INFINITY, S = 0.f, TL = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) M = fmaxf(M, mk[k][u]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (k < t) {
+          S += sk[k][u] * __expf(mk[k][u] - M);
+          TL += tk[k][u];
+        }
+      }
+      const float w = mask ? (float)mask[r] : 1.f;
+      const float l = M + __logf(S);
+      const float lr = w * (l - TL);
+      lse[r] = l;
+      loss_rows[r] = lr;
+      acc += lr;
+      cnt += w;
+    }
+  }
+  __shared__ float sa[16], sc[16];
+  acc = wave_sum(acc);
+  cnt = wave_sum(cnt);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sa[wave] = acc; sc[wave] = cnt; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float A = 0.f, C = 0.f;
+    for (int w = 0; w < 16; ++w) { A += sa[w]; C += sc[w]; }
+    loss[0] = C > 0.f ? A / C : 0.f;
+    loss[1] = C;
+  }
+}
+
 // In place: l <- g (exp(l - lse) - [j == target - v0]), g = dloss * mask / count.
 // Streams the [rows][vr] logits as one flat array of 16-B chunks (kU chunks
 // per thread, loads issued together); the per-row scalars are re-read per
@@ -259,7 +321,10 @@ hipError_t launch_xent_finish(const float* const* all_stats, int t, int64_t rows
   TraceScope trace(K_XENT_FINISH, s, (double)rows * (12.0 * t + 9));
   StatPtrs sp;
   for (int i = 0; i < 64; ++i) sp.p[i] = i < t ? all_stats[i] : nullptr;
-  hipLaunchKernelGGL(xent_finish_kernel, dim3(1), dim3(1024), 0, s, sp, t, rows, mask, lse, loss_rows, loss);
+  if (t <= 8)
+    hipLaunchKernelGGL(xent_finish8_kernel, dim3(1), dim3(1024), 0, s, sp, t, rows, mask, lse, loss_rows, loss);
+  else
+    hipLaunchKernelGGL(xent_finish_kernel, dim3(1), dim3(1024), 0, s, sp, t, rows, mask, lse, loss_rows, loss);
   return hipGetLastError();
 }
 
