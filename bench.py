@@ -99,11 +99,11 @@ def standin_sum_ms(st, passes, B):
     return sum(ms for name, ms, _ in recs if name == "partial_sum") / passes
 
 
-def roofline(agg, dtype):
+def roofline(agg, dtype, workload):
     if not agg:   # no traced steps (--trace-steps 0)
         return None
     name, (count, ms, work) = max(agg.items(), key=lambda kv: kv[1][1])
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name, workload)
     if name in MFMA_KERNELS:
         achieved = work / (ms / 1e3) / 1e12
         peak = PEAK_TFLOPS[dtype]
@@ -335,13 +335,17 @@ def summarize_profiles(d: str, workload: str):
     print(f"wrote profiles for {workload}")
 
 
-def measured_traffic(family: str):
+def measured_traffic(family: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None if the
-    kernel's source changed since the counters were taken."""
+    counters were taken on another workload or the kernel's source changed
+    since."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
-        rec = json.load(open(path))["kernels"][family]
+        doc = json.load(open(path))
+        rec = doc["kernels"][family]
     except (OSError, KeyError, ValueError):
+        return None
+    if doc.get("workload") != workload:
         return None
     return rec["bytes_per_launch"] if rec.get("source_sha256") == source_sha(family) else None
 
@@ -432,7 +436,7 @@ def main():
                 "note": "the rank's own calls: layer time minus the event-timed shard_partial_sum launches "
                         "(stand-ins for the all-reduce on t GPUs)"}},
         "loss": round(loss, 6),
-        "roofline": roofline(agg, cfg.dtype),
+        "roofline": roofline(agg, cfg.dtype, cfg.name),
         "embedding": emb,
         "recompute": rec,
         "kernels_per_step": [{"kernel": k, "launches": c // args.trace_steps, "ms": round(t, 4),
