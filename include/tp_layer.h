@@ -212,6 +212,25 @@ tpl_status vocab_parallel_xent_fwd(const tpl_desc* desc, tpl_xent_phase phase,
  * tokens: [N] int32 global ids (ids outside [0, V) contribute nothing);
  * emb_in: E_r [V_r][h] storage dtype; workspace: device scratch of
  * vocab_parallel_embedding_ws_bytes(desc) bytes, overwritten. */
+/* Loss rows of a masked loss (podcast page, Outline: the large-BERT variant;
+ * its masked-token loss is taken on a fraction of the positions). The loss
+ * needs logits, dlogits, dH and dE only for those rows, so a caller that knows
+ * them (the batch's mask gives their index list) gathers them, runs
+ * vocab_parallel_xent_fwd/bwd on a descriptor of that many rows with
+ * loss_mask NULL (the mean over the gathered rows is the masked mean), and
+ * expands dH back to every row.
+ *   tpl_rows_gather: dst row i = src row rows[i], i < n.
+ *   tpl_rows_expand: dst row r = src row pos[r] if pos[r] >= 0, else zeros,
+ *     r < n_dst (pos[r] = index of row r in the gathered list, or -1).
+ * src: n_src rows of row_bytes bytes (a multiple of 4); an index outside
+ * [0, n_src) reads nothing and gives a zero row. rows / pos: int32 device
+ * arrays. Pointers 4-byte aligned; INVALID_ARG for negative sizes or a bad
+ * row_bytes, before any launch. */
+tpl_status tpl_rows_gather(const void* src, int64_t n_src, const int32_t* rows, int64_t n, int64_t row_bytes,
+                           void* dst, void* stream);
+tpl_status tpl_rows_expand(const void* src, int64_t n_src, const int32_t* pos, int64_t n_dst, int64_t row_bytes,
+                           void* dst, void* stream);
+
 size_t vocab_parallel_embedding_ws_bytes(const tpl_desc* desc);
 tpl_status vocab_parallel_embedding_fwd(const tpl_desc* desc, const int32_t* tokens, const void* emb_in,
                                         void* x_partial, void* stream);

@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.vocab_parallel_xent_bwd.argtypes = [P(TplDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_float,
                                               _VP, _VP, _VP]
         L.tpl_gemm.argtypes = [_I32, _I32, _I32, _I64, _I64, _I64, _VP, _I64, _VP, _I64, _VP, _VP, _I64, _I32, _VP]
+        L.tpl_rows_gather.argtypes = [_VP, ctypes.c_int64, _VP, ctypes.c_int64, ctypes.c_int64, _VP, _VP]
+        L.tpl_rows_gather.restype = _I32
+        L.tpl_rows_expand.argtypes = [_VP, ctypes.c_int64, _VP, ctypes.c_int64, ctypes.c_int64, _VP, _VP]
+        L.tpl_rows_expand.restype = _I32
         L.tpl_trace_enable.argtypes = [_I32]
         L.tpl_trace_enable.restype = _I32
         L.tpl_trace_read.argtypes = [P(ctypes.c_int32), P(ctypes.c_float), P(ctypes.c_double), _I32]
@@ -95,7 +99,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("tp_layer_saved_bytes", "tp_layer_shard_fwd", "shard_partial_sum", "tp_layer_shard_bwd",
             "vocab_parallel_xent_stats_bytes", "vocab_parallel_xent_fwd",
-            "vocab_parallel_embedding_ws_bytes", "vocab_parallel_embedding_fwd", "vocab_parallel_embedding_bwd", "vocab_parallel_xent_bwd", "tpl_gemm", "tpl_trace_enable",
+            "vocab_parallel_embedding_ws_bytes", "vocab_parallel_embedding_fwd", "vocab_parallel_embedding_bwd", "vocab_parallel_xent_bwd", "tpl_rows_gather", "tpl_rows_expand", "tpl_gemm", "tpl_trace_enable",
             "tpl_trace_read", "tpl_trace_kernel_name", "tpl_status_string")
 
 
@@ -197,6 +201,16 @@ def vocab_parallel_xent_bwd(desc, hidden, emb, targets, loss_mask, logits, lse, 
     _check("vocab_parallel_xent_bwd", lib().vocab_parallel_xent_bwd(
         ctypes.byref(desc), _ptr(hidden), _ptr(emb), _ptr(targets), _ptr(loss_mask), _ptr(logits), _ptr(lse),
         _ptr(loss), float(dloss), _ptr(d_hidden_partial), _ptr(d_emb), _stream(stream)))
+
+
+def tpl_rows_gather(src, n_src, rows, n, row_bytes, dst, stream=None):
+    _check("tpl_rows_gather", lib().tpl_rows_gather(_ptr(src), n_src, _ptr(rows), n, row_bytes, _ptr(dst),
+                                                    _stream(stream)))
+
+
+def tpl_rows_expand(src, n_src, pos, n_dst, row_bytes, dst, stream=None):
+    _check("tpl_rows_expand", lib().tpl_rows_expand(_ptr(src), n_src, _ptr(pos), n_dst, row_bytes, _ptr(dst),
+                                                    _stream(stream)))
 
 
 def tpl_gemm(dtype, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, bias, C, ldc, c_f32, stream=None):

@@ -155,7 +155,8 @@ int g_trace_cap = 0, g_trace_used = 0;
 const char* const kKernelNames[K_COUNT] = {
     "gemm_nt", "gemm_nn", "gemm_tn", "attn_fwd", "attn_bwd_pre", "attn_bwd_dq", "attn_bwd_dkdv",
     "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_cols", "colsum", "colsum_final", "partial_sum",
-    "xent_stats", "xent_finish", "xent_dlogits", "xent_merge", "embedding_fwd", "embedding_sort", "embedding_bwd"};
+    "xent_stats", "xent_finish", "xent_dlogits", "xent_merge", "embedding_fwd", "embedding_sort", "embedding_bwd",
+    "rows_gather", "rows_expand"};
 
 }  // namespace
 
@@ -489,6 +490,23 @@ tpl_status vocab_parallel_embedding_bwd(const tpl_desc* desc, const int32_t* tok
   if (!ok_ptr(tokens) || !ok_ptr(d_out) || !ok_ptr(d_emb_in) || !ok_ptr(workspace)) return TPL_ERR_INVALID_ARG;
   return from_hip(launch_embedding_bwd(m.dt, tokens, d_out, d_emb_in, m.N, (int)m.h, (int64_t)desc->rank * m.vr,
                                        (int)m.vr, workspace, static_cast<hipStream_t>(stream)));
+}
+
+static bool ok_ptr4(const void* p) { return p != nullptr && reinterpret_cast<uintptr_t>(p) % 4 == 0; }
+
+tpl_status tpl_rows_gather(const void* src, int64_t n_src, const int32_t* rows, int64_t n, int64_t row_bytes, void* dst,
+                           void* stream) {
+  if (n < 0 || n_src < 0 || row_bytes <= 0 || row_bytes % 4 || n >= (1LL << 40) / row_bytes) return TPL_ERR_INVALID_ARG;
+  if (n > 0 && (!ok_ptr4(rows) || !ok_ptr4(dst) || (n_src > 0 && !ok_ptr4(src)))) return TPL_ERR_INVALID_ARG;
+  return from_hip(tpl::launch_rows_gather(src, rows, n, n_src, row_bytes, dst, static_cast<hipStream_t>(stream)));
+}
+
+tpl_status tpl_rows_expand(const void* src, int64_t n_src, const int32_t* pos, int64_t n_dst, int64_t row_bytes,
+                           void* dst, void* stream) {
+  if (n_dst < 0 || n_src < 0 || row_bytes <= 0 || row_bytes % 4 || n_dst >= (1LL << 40) / row_bytes)
+    return TPL_ERR_INVALID_ARG;
+  if (n_dst > 0 && (!ok_ptr4(pos) || !ok_ptr4(dst) || (n_src > 0 && !ok_ptr4(src)))) return TPL_ERR_INVALID_ARG;
+  return from_hip(tpl::launch_rows_expand(src, pos, n_dst, n_src, row_bytes, dst, static_cast<hipStream_t>(stream)));
 }
 
 tpl_status tpl_gemm(int32_t dtype, int32_t a_kmajor, int32_t b_kmajor, int64_t M, int64_t N, int64_t K, const void* A,

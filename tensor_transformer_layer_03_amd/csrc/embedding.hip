@@ -218,4 +218,85 @@ hipError_t launch_embedding_bwd(int dtype, const int32_t* tokens, const void* d_
   return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------------ loss rows
+// Gather of the rows a masked loss is taken on, and the expansion of their
+// gradient back to every row (zeros elsewhere). One thread per W-byte unit
+// (W = 16 when the rows and pointers allow, else 4); every index is checked
+// against the source's row count, so a bad index reads nothing.
+namespace {
+template <int W>
+struct Unit;
+template <>
+struct Unit<16> { using T = u32x4; };
+template <>
+struct Unit<4> { using T = uint32_t; };
+
+template <int W>
+__global__ __launch_bounds__(256) void rows_gather_kernel(const char* __restrict__ src, const int32_t* __restrict__ rows,
+                                                          int64_t n, int64_t n_src, int64_t row_bytes,
+                                                          char* __restrict__ dst) {
+  using U = typename Unit<W>::T;
+  const int64_t upr = row_bytes / W;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= n * upr) return;
+  const int64_t i = u / upr, c = u % upr;
+  const int64_t r = rows[i];
+  U v{};
+  if (r >= 0 && r < n_src) v = *reinterpret_cast<const U*>(src + r * row_bytes + c * W);
+  *reinterpret_cast<U*>(dst + i * row_bytes + c * W) = v;
+}
+
+template <int W>
+__global__ __launch_bounds__(256) void rows_expand_kernel(const char* __restrict__ src, const int32_t* __restrict__ pos,
+                                                          int64_t n_dst, int64_t n_src, int64_t row_bytes,
+                                                          char* __restrict__ dst) {
+  using U = typename Unit<W>::T;
+  const int64_t upr = row_bytes / W;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= n_dst * upr) return;
+  const int64_t r = u / upr, c = u % upr;
+  const int64_t p = pos[r];
+  U v{};
+  if (p >= 0 && p < n_src) v = *reinterpret_cast<const U*>(src + p * row_bytes + c * W);
+  *reinterpret_cast<U*>(dst + r * row_bytes + c * W) = v;
+}
+
+bool wide_units(const void* a, const void* b, int64_t row_bytes) {
+  return row_bytes % 16 == 0 && reinterpret_cast<uintptr_t>(a) % 16 == 0 && reinterpret_cast<uintptr_t>(b) % 16 == 0;
+}
+}  // namespace
+
+hipError_t launch_rows_gather(const void* src, const int32_t* rows, int64_t n, int64_t n_src, int64_t row_bytes,
+                              void* dst, hipStream_t s) {
+  TraceScope trace(K_ROWS_GATHER, s, 2.0 * (double)n * row_bytes + 4.0 * n);
+  if (n == 0) return hipSuccess;
+  const bool w16 = wide_units(src, dst, row_bytes);
+  const int64_t units = n * (row_bytes / (w16 ? 16 : 4));
+  const dim3 grid((unsigned)((units + 255) / 256));
+  if (w16)
+    hipLaunchKernelGGL(rows_gather_kernel<16>, grid, dim3(256), 0, s, static_cast<const char*>(src), rows, n, n_src,
+                       row_bytes, static_cast<char*>(dst));
+  else
+    hipLaunchKernelGGL(rows_gather_kernel<4>, grid, dim3(256), 0, s, static_cast<const char*>(src), rows, n, n_src,
+                       row_bytes, static_cast<char*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_expand(const void* src, const int32_t* pos, int64_t n_dst, int64_t n_src, int64_t row_bytes,
+                              void* dst, hipStream_t s) {
+  TraceScope trace(K_ROWS_EXPAND, s, (double)n_dst * row_bytes + (double)n_src * row_bytes + 4.0 * n_dst);
+  if (n_dst == 0) return hipSuccess;
+  const bool w16 = wide_units(src, dst, row_bytes);
+  const int64_t units = n_dst * (row_bytes / (w16 ? 16 : 4));
+  const dim3 grid((unsigned)((units + 255) / 256));
+  if (w16)
+    hipLaunchKernelGGL(rows_expand_kernel<16>, grid, dim3(256), 0, s, static_cast<const char*>(src), pos, n_dst, n_src,
+                       row_bytes, static_cast<char*>(dst));
+  else
+    hipLaunchKernelGGL(rows_expand_kernel<4>, grid, dim3(256), 0, s, static_cast<const char*>(src), pos, n_dst, n_src,
+                       row_bytes, static_cast<char*>(dst));
+  return hipGetLastError();
+}
+
 }  // namespace tpl

@@ -14,6 +14,7 @@ enum KernelId {
   K_GEMM_NT = 0, K_GEMM_NN, K_GEMM_TN, K_ATTN_FWD, K_ATTN_BWD_PRE, K_ATTN_BWD_DQ,
   K_ATTN_BWD_DKDV, K_LN_FWD, K_LN_BWD, K_LN_BWD_COLS, K_COLSUM, K_COLSUM_FINAL,
   K_PARTIAL_SUM, K_XENT_STATS, K_XENT_FINISH, K_XENT_DLOGITS, K_XENT_MERGE, K_EMB_FWD, K_EMB_SORT, K_EMB_BWD,
+  K_ROWS_GATHER, K_ROWS_EXPAND,
   K_COUNT
 };
 const char* kernel_name(int id);
@@ -125,6 +126,13 @@ hipError_t launch_xent_dlogits(int dtype, void* logits, int64_t rows, int vr,
 // ------------------------------------------------------------------ input embedding
 // Workspace bytes of the backward (sort keys / values twice, segment starts).
 size_t embedding_ws_bytes(int64_t rows, int vr);
+// Row gather / expand of a masked loss's rows (row_bytes a multiple of 4):
+// gather: dst[i] = src[rows[i]] (i < n; an index outside [0, n_src) gives zeros);
+// expand: dst[r] = src[pos[r]] if 0 <= pos[r] < n_src, else zeros (r < n_dst).
+hipError_t launch_rows_gather(const void* src, const int32_t* rows, int64_t n, int64_t n_src, int64_t row_bytes,
+                              void* dst, hipStream_t s);
+hipError_t launch_rows_expand(const void* src, const int32_t* pos, int64_t n_dst, int64_t n_src, int64_t row_bytes,
+                              void* dst, hipStream_t s);
 hipError_t launch_embedding_fwd(int dtype, const int32_t* tokens, const void* emb, void* out, int64_t rows, int cols,
                                 int64_t v0, int vr, hipStream_t s);
 hipError_t launch_embedding_bwd(int dtype, const int32_t* tokens, const void* d_out, float* d_emb, int64_t rows,

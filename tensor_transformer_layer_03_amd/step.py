@@ -92,18 +92,41 @@ class LayerStep:
             "d_b_o": z(h, dtype=torch.float32), "d_ln2_g": z(h, dtype=torch.float32),
             "d_ln2_b": z(h, dtype=torch.float32), "d_b_2": z(h, dtype=torch.float32),
         }
+        # A masked loss runs on its rows only: their index list (from the
+        # batch's mask) gathers them, the loss sees a descriptor of that many
+        # rows, and dH is expanded back to every row with zeros elsewhere.
+        self.loss_idx = None
+        self.NL = N
+        if cfg.mask_rows is not None:
+            idx = np.nonzero(rep.mask)[0].astype(np.int32)
+            pos = np.full(N, -1, np.int32)
+            pos[idx] = np.arange(len(idx), dtype=np.int32)
+            self.loss_idx = idx
+            self.NL = len(idx)
+            self.shared.update({
+                "loss_rows_idx": torch.from_numpy(idx).to(self.device),
+                "loss_rows_pos": torch.from_numpy(pos).to(self.device),
+                "out_l": z(self.NL, h), "targets_l": torch.empty(self.NL, dtype=torch.int32, device=self.device),
+                "lse": z(self.NL, dtype=torch.float32), "loss_rows": z(self.NL, dtype=torch.float32),
+            })
         self.peers = [D(p) for p in peers]
         self.peer_stats = [torch.from_numpy(np.ascontiguousarray(s, np.float32)).to(self.device) for s in peer_stats]
+        if self.loss_idx is not None:   # the stand-in ranks' statistics of the loss rows
+            self.peer_stats = [self._gather(ps, N, 12, torch.empty(self.NL, 3, dtype=torch.float32, device=self.device))
+                               for ps in self.peer_stats]
         self.states: list[RankState] = []
         for r in self.ranks:
             hs = shards[r]
             desc = B.make_desc(cfg.hidden, cfg.heads, cfg.head_dim, cfg.ffn, cfg.tp, r, cfg.seq, cfg.micro_batch,
                                cfg.vocab, cfg.causal, dt, cfg.ln_eps)
+            xdesc = desc if self.loss_idx is None else B.make_desc(
+                cfg.hidden, cfg.heads, cfg.head_dim, cfg.ffn, cfg.tp, r, self.NL, 1, cfg.vocab, cfg.causal, dt,
+                cfg.ln_eps)   # the loss's rows
             hr, fr, vr = cfg.hidden // cfg.tp, cfg.ffn // cfg.tp, cfg.vocab // cfg.tp
             t = {k: _dev(v, dt, self.device) for k, v in hs.items()}
             sa = B.tp_layer_saved_bytes(desc, B.TPL_BLOCK_ATTN)
             sm = B.tp_layer_saved_bytes(desc, B.TPL_BLOCK_MLP)
-            sx = B.vocab_parallel_xent_stats_bytes(desc)
+            sx = B.vocab_parallel_xent_stats_bytes(xdesc)
             if sa == 0 or sm == 0 or sx == 0:
                 raise ValueError(f"workload rejected by tp_layer_saved_bytes (rank {r})")
             f32 = torch.float32
@@ -111,18 +134,24 @@ class LayerStep:
                 "saved_attn": torch.empty(sa, dtype=torch.uint8, device=self.device),
                 "saved_mlp": torch.empty(sm, dtype=torch.uint8, device=self.device),
                 "part_attn": z(N, h), "part_mlp": z(N, h), "dln_attn": z(N, h), "dln_mlp": z(N, h),
-                "logits": z(N, vr), "stats_buf": z(sx // 4, dtype=f32), "dH": z(N, h),
+                "logits": z(self.NL, vr), "stats_buf": z(sx // 4, dtype=f32), "dH": z(N, h),
+                "dH_l": z(self.NL, h) if self.loss_idx is not None else None,
                 "d_w_qkv": z(3 * hr, h, dtype=f32), "d_b_qkv": z(3 * hr, dtype=f32), "d_w_o": z(h, hr, dtype=f32),
                 "d_w_1": z(fr, h, dtype=f32), "d_b_1": z(fr, dtype=f32), "d_w_2": z(h, fr, dtype=f32),
                 "d_emb": z(vr, h, dtype=f32),
             })
             sh = self.shared
             attn = B.block_params(sh["ln1_g"], sh["ln1_b"], t["w_qkv"], t["b_qkv"], t["w_o"])
-            t["stats"] = t["stats_buf"][:N * 3].view(N, 3)   # the exchanged part; the rest is scratch
+            t["stats"] = t["stats_buf"][:self.NL * 3].view(self.NL, 3)   # the exchanged part; the rest is scratch
+            t["xdesc"] = xdesc
             mlp = B.block_params(sh["ln2_g"], sh["ln2_b"], t["w_1"], t["b_1"], t["w_2"])
             self.states.append(RankState(r, desc, attn, mlp, t))
         self.exchanges = 0
         self.dloss = 1.0
+
+    def _gather(self, src, n_src, row_bytes, dst, stream=None):
+        B.tpl_rows_gather(src, n_src, self.shared["loss_rows_idx"], self.NL, row_bytes, dst, stream)
+        return dst
 
     # -------------------------------------------------------------- exchanges
     def _sum(self, key, bias, residual, out, stream=None):
@@ -144,17 +173,29 @@ class LayerStep:
                                  st.tensors["saved_mlp"], stream)
         self._sum("part_mlp", sh["b_2"], sh["h1"], sh["out"], stream)
 
+    def _loss_inputs(self):
+        """(hidden, targets) of the loss's rows: the whole batch, or the masked
+        rows gathered (a NULL mask then: the mean over them is the masked mean)."""
+        sh = self.shared
+        if self.loss_idx is None:
+            return sh["out"], sh["targets"]
+        return sh["out_l"], sh["targets_l"]
+
     def xent_forward(self, stream=None):
         sh = self.shared
-        mask = sh["mask"] if self.cfg.mask_rows is not None else None
+        if self.loss_idx is not None:
+            es = 2 if self.cfg.dtype == "bf16" else 4
+            self._gather(sh["out"], self.N, self.cfg.hidden * es, sh["out_l"], stream)
+            self._gather(sh["targets"], self.N, 4, sh["targets_l"], stream)
+        hidden, targets = self._loss_inputs()
         for st in self.states:
-            B.vocab_parallel_xent_fwd(st.desc, B.TPL_XENT_LOCAL, hidden=sh["out"], emb=st.tensors["emb"],
-                                      targets=sh["targets"], loss_mask=mask, logits=st.tensors["logits"],
+            B.vocab_parallel_xent_fwd(st.tensors["xdesc"], B.TPL_XENT_LOCAL, hidden=hidden, emb=st.tensors["emb"],
+                                      targets=targets, loss_mask=None, logits=st.tensors["logits"],
                                       stats=st.tensors["stats"], stream=stream)
         all_stats = self._stats_in_rank_order()
-        B.vocab_parallel_xent_fwd(self.states[0].desc, B.TPL_XENT_FINISH, targets=sh["targets"], loss_mask=mask,
-                                  all_stats=all_stats, lse=sh["lse"], loss_rows=sh["loss_rows"], loss=sh["loss"],
-                                  stream=stream)
+        B.vocab_parallel_xent_fwd(self.states[0].tensors["xdesc"], B.TPL_XENT_FINISH, targets=targets,
+                                  loss_mask=None, all_stats=all_stats, lse=sh["lse"], loss_rows=sh["loss_rows"],
+                                  loss=sh["loss"], stream=stream)
 
     def _stats_in_rank_order(self):
         mine = {st.rank: st.tensors["stats"] for st in self.states}
@@ -163,11 +204,15 @@ class LayerStep:
 
     def xent_backward(self, stream=None):
         sh = self.shared
-        mask = sh["mask"] if self.cfg.mask_rows is not None else None
+        hidden, targets = self._loss_inputs()
         for st in self.states:
-            B.vocab_parallel_xent_bwd(st.desc, sh["out"], st.tensors["emb"], sh["targets"], mask,
-                                      st.tensors["logits"], sh["lse"], sh["loss"], self.dloss, st.tensors["dH"],
-                                      st.tensors["d_emb"], stream)
+            t = st.tensors
+            dh = t["dH"] if self.loss_idx is None else t["dH_l"]
+            B.vocab_parallel_xent_bwd(t["xdesc"], hidden, t["emb"], targets, None, t["logits"], sh["lse"],
+                                      sh["loss"], self.dloss, dh, t["d_emb"], stream)
+            if self.loss_idx is not None:   # dH of the loss rows back to every row, zeros elsewhere
+                es = 2 if self.cfg.dtype == "bf16" else 4
+                B.tpl_rows_expand(dh, self.NL, sh["loss_rows_pos"], self.N, self.cfg.hidden * es, t["dH"], stream)
         self._sum("dH", None, sh["R"], sh["dout"], stream)
 
     def poison_saved(self):
@@ -211,9 +256,10 @@ class LayerStep:
     def results(self) -> dict:
         """Every output of the pass as host float64 numpy arrays."""
         f = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
-        out = {k: f(v) for k, v in self.shared.items() if k not in ("targets", "mask")}
+        skip = ("targets", "mask", "loss_rows_idx", "loss_rows_pos", "out_l", "targets_l")
+        out = {k: f(v) for k, v in self.shared.items() if k not in skip}
         for st in self.states:
             for k, v in st.tensors.items():
-                if k.startswith(("d_", "part_", "dln_", "dH")) or k == "stats":
+                if (k.startswith(("d_", "part_", "dln_")) or k in ("dH", "stats")) and v is not None:
                     out[f"{k}@{st.rank}"] = f(v)
         return out

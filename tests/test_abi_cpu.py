@@ -100,3 +100,19 @@ def test_null_and_misaligned_pointers_are_rejected():
 def test_status_strings():
     assert B.status_string(B.TPL_OK) == "ok"
     assert "unsupported" in B.status_string(B.TPL_ERR_UNSUPPORTED)
+
+
+@pytest.mark.parametrize("args", [
+    (16, 10, 16, -1, 12, 16),    # negative row count
+    (16, -1, 16, 4, 12, 16),     # negative source rows
+    (16, 10, 16, 4, 0, 16),      # empty rows
+    (16, 10, 16, 4, 6, 16),      # row bytes not a multiple of 4
+    (16, 10, None, 4, 12, 16),   # no index list
+    (16, 10, 16, 4, 12, None),   # no destination
+    (16, 10, 18, 4, 12, 16),     # misaligned index list
+])
+def test_row_gather_and_expand_reject_bad_arguments(args):
+    """Rejected on the host, before any launch (no device is touched)."""
+    L = B.lib()
+    assert L.tpl_rows_gather(*args, None) == B.TPL_ERR_INVALID_ARG
+    assert L.tpl_rows_expand(*args, None) == B.TPL_ERR_INVALID_ARG
