@@ -68,6 +68,21 @@ def time_loop(fn, steps, torch):
     return start.elapsed_time(end) / steps
 
 
+def step_percentiles(fn, steps, torch):
+    """Per-step milliseconds (an event pair per step on the current stream):
+    p10, median, p90."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+    return {"p10": round(q(0.1), 4), "median": round(q(0.5), 4), "p90": round(q(0.9), 4), "steps": steps}
+
+
 def traced_kernels(st, steps, B, dtype):
     """Per-kernel event timing of `steps` passes: {name: (launches, ms, work)}."""
     import torch
@@ -176,6 +191,8 @@ PROFILE_CMDS = {
            "-- python3 <repo>/bench.py --steps 2 --warmup 1 --cpu-seqs 0 --trace-steps 1 --no-layer-only",
     "copy": "cd /tmp && rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <out>/pmc_<counter> -o copy "
             "-- python3 <repo>/bench.py --copy-calibration",
+    "mfma": "cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES --output-format csv -d <out>/pmc_mfma "
+            "-o bench -- python3 <repo>/bench.py --steps 2 --warmup 1 --cpu-seqs 0 --trace-steps 1 --no-layer-only",
 }
 
 
@@ -332,6 +349,21 @@ def summarize_profiles(d: str, workload: str):
         lines.append(f"| {f} | {v['fetch_bytes_per_launch'] / 1e6:.1f} | {v['write_bytes_per_launch'] / 1e6:.1f} | "
                      f"{v['source_sha256']} |")
     open(os.path.join(prof, f"hbm_traffic_{workload}.md"), "w").write("\n".join(lines) + "\n")
+    mfma_dir = os.path.join(d, "pmc_mfma")
+    if os.path.isdir(mfma_dir):
+        busy = collections.defaultdict(lambda: [0.0, 0.0])
+        for r in csv.DictReader(open(os.path.join(mfma_dir, "bench_counter_collection.csv"))):
+            f = kernel_family(r["Kernel_Name"])
+            busy[f][0 if r["Counter_Name"] == "SQ_VALU_MFMA_BUSY_CYCLES" else 1] += float(r["Counter_Value"])
+        lines = [f"# MFMA busy share per kernel family, {workload} (rocprofv3 --pmc)", "",
+                 "Command:", "", "    " + PROFILE_CMDS["mfma"], "",
+                 "share = SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES), summed over the family's dispatches:",
+                 "the fraction of SIMD cycles (4 SIMDs per CU) with the matrix unit busy while the CUs are busy.", "",
+                 "| family | MFMA busy share |", "|---|---|"]
+        for f, (mb, cu) in sorted(busy.items(), key=lambda kv: -kv[1][0]):
+            if mb > 0:
+                lines.append(f"| {f} | {mb / (4 * cu):.3f} |")
+        open(os.path.join(prof, f"mfma_busy_{workload}.md"), "w").write("\n".join(lines) + "\n")
     print(f"wrote profiles for {workload}")
 
 
@@ -395,6 +427,7 @@ def main():
     ms = time_loop(st.step, args.steps, torch)
     ms_layer = (time_loop(lambda: (st.forward(), st.backward()), max(3, args.steps // 2), torch)
                 if args.layer_only else None)
+    pct = step_percentiles(st.step, args.steps, torch)
     sums_ms = standin_sum_ms(st, 3, B) if args.layer_only else None
     agg = traced_kernels(st, args.trace_steps, B, cfg.dtype)
     loss = float(st.shared["loss"][0].item())
@@ -412,6 +445,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms_percentiles": pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
