@@ -406,15 +406,20 @@ struct TileReg {
 // Loads of K-tile KT_ of both operands (into stage S_ for the direct-to-LDS
 // path, into registers otherwise); past the last tile the buffers are
 // zero-length (nothing is read, zeros are produced).
+// K-major operands: the range ends at the last valid element of the tile's
+// last row (((rows - 1) * ld + K) elements from the first row's start), so
+// the reads of a ragged last K-tile stop at the operand's end also when a
+// K split has moved the base K columns in.
 #define TPL_TILE_ARGS_A(KT_)                                                                              \
   (A_K ? g.A + (int64_t)m0 * g.lda * 2 : g.A + (int64_t)(KT_) * 64 * g.lda * 2),                         \
-      ((KT_) * 64 < g.K ? (A_K ? (int64_t)(g.M - m0) * g.lda * 2                                          \
+      ((KT_) * 64 < g.K ? (A_K ? ((int64_t)(g.M - m0 - 1) * g.lda + g.K) * 2                            \
                                : (int64_t)(g.K - (KT_) * 64) * g.lda * 2 - g.a_trim)                      \
                         : 0),                                                                            \
       (A_K ? (KT_) * 128 : 0)
 #define TPL_TILE_ARGS_B(KT_)                                                                              \
   (B_K ? g.B + (int64_t)n0 * g.ldb * 2 : g.B + (int64_t)(KT_) * 64 * g.ldb * 2),                         \
-      ((KT_) * 64 < g.K ? (B_K ? (int64_t)(g.N - n0) * g.ldb * 2 : (int64_t)(g.K - (KT_) * 64) * g.ldb * 2) \
+      ((KT_) * 64 < g.K ? (B_K ? ((int64_t)(g.N - n0 - 1) * g.ldb + g.K) * 2                            \
+                               : (int64_t)(g.K - (KT_) * 64) * g.ldb * 2)                                 \
                         : 0),                                                                            \
       (B_K ? (KT_) * 128 : 0)
 #define TPL_ISSUE_TILES(KT_, S_)                                   \

@@ -111,6 +111,10 @@ WIDE = [
     # bf16-rounded logits alone put the loss gradient ~1.5% off the float64 oracle
     synth.tiny_config("bf16", hidden=1280, heads=10, head_dim=128, ffn=2560, tp=2, seq=33, micro_batch=2,
                       vocab=256, causal=False, sigma_w=0.02, index=57, name="small_bf16_wide_rows"),
+    # 23 heads x 96: the output projection's input gradient ([128, 2208], K = 2208) splits over K in
+    # two, the last split 1056 deep, so its last K-tile is ragged at a moved base
+    synth.tiny_config("bf16", hidden=2208, heads=23, head_dim=96, ffn=4416, tp=1, seq=64, micro_batch=2,
+                      vocab=256, causal=True, sigma_w=0.02, index=58, name="small_bf16_split_ragged_k"),
 ]
 
 
