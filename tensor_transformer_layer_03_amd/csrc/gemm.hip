@@ -972,7 +972,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
   tB.init(g.ldb, wave, lane);
   const char* baseA = g.A + (int64_t)m0 * g.lda * 2;
   const char* baseB = g.B + (int64_t)n0 * g.ldb * 2;
-  const int64_t bytesA = (int64_t)(g.M - m0) * g.lda * 2, bytesB = (int64_t)(g.N - n0) * g.ldb * 2;
+  // ranges end at the last valid element of the tile's last row (a ragged last
+  // K-tile reads nothing past the operand)
+  const int64_t bytesA = ((int64_t)(g.M - m0 - 1) * g.lda + g.K) * 2;
+  const int64_t bytesB = ((int64_t)(g.N - n0 - 1) * g.ldb + g.K) * 2;
 #define TPL_MS_ISSUE(KT_)                                                                                \
   do {                                                                                                   \
     const bool live_ = (KT_) * 32 < g.K;                                                                 \
