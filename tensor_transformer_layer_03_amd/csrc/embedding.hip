@@ -121,6 +121,124 @@ __global__ __launch_bounds__(256) void embed_segments_kernel(const uint32_t* __r
   if (k < (uint32_t)vr && (i == 0 || keys[i - 1] != k)) seg[k] = i;
 }
 
+// In-LDS sort for up to kLdsSortMax rows, one workgroup of 1024 threads, in
+// one launch that also derives the keys from the ids and writes seg[]. Each
+// row becomes one 32-bit word (key << ib) | row, ib = bits of the largest row
+// index; the words are all distinct, so ordering them by key alone, stably,
+// is the same as ordering (key, row) pairs. LSD radix passes over the key in
+// 4-bit digits; between passes thread t holds rows [E*t, E*t + E) in order
+// (E = ceil(n / 1024) <= 8) in registers. In a pass each thread counts its
+// digits in a 64-bit word of 4-bit counters (an element's rank among its
+// thread's equal digits is the counter before the increment), the 16 x 1024
+// counts, digit-major then thread, are scanned across the workgroup, and
+// every element goes to base[digit][thread] + rank in LDS: stable, since the
+// scan order is the element order within each digit. Global loads and stores
+// run in the coalesced order j = tid + 1024 q through LDS. seg[] is written
+// at the first occurrence of each key present only; the gradient kernel
+// accepts an entry only where it points at that first occurrence, so the
+// other entries are never cleared.
+constexpr int kLdsSortMax = 8192, kLdsSortE = kLdsSortMax / kSortThreads;
+__global__ __launch_bounds__(kSortThreads) void embed_sort_lds_kernel(const int32_t* __restrict__ tok, int n,
+                                                                      int64_t v0, int vr, int ib, int passes,
+                                                                      uint32_t* __restrict__ keys,
+                                                                      uint32_t* __restrict__ vals,
+                                                                      int32_t* __restrict__ seg) {
+  __shared__ uint32_t buf[kLdsSortMax];
+  __shared__ __attribute__((aligned(16))) uint32_t cnt[16 * kSortThreads];   // [digit][thread]
+  __shared__ __attribute__((aligned(16))) uint32_t wsum[kSortWaves];
+  if (n <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t t8[kLdsSortE];
+#pragma unroll
+  for (int q = 0; q < kLdsSortE; ++q) t8[q] = tok[min(tid + q * kSortThreads, n - 1)];
+#pragma unroll
+  for (int q = 0; q < kLdsSortE; ++q) {
+    const int j = tid + q * kSortThreads;
+    const int64_t key = (int64_t)t8[q] - v0;
+    const uint32_t k = (key >= 0 && key < vr) ? (uint32_t)key : (uint32_t)vr;
+    if (j < n) buf[j] = (k << ib) | (uint32_t)j;
+  }
+  __syncthreads();
+  const int E = (n + kSortThreads - 1) / kSortThreads;
+  const int first = tid * E;
+  const int own = max(0, min(E, n - first));   // rows this thread holds
+  uint32_t w[kLdsSortE];
+#pragma unroll
+  for (int e = 0; e < kLdsSortE; ++e) w[e] = buf[min(first + e, n - 1)];
+  for (int p = 0; p < passes; ++p) {
+    const int shift = ib + 4 * p;
+    uint64_t c = 0;
+    uint32_t rk[kLdsSortE];
+#pragma unroll
+    for (int e = 0; e < kLdsSortE; ++e) {
+      const int d4 = (int)((w[e] >> shift) & 15u) * 4;
+      rk[e] = (uint32_t)(c >> d4) & 15u;
+      if (e < own) c += 1ull << d4;
+    }
+#pragma unroll
+    for (int d = 0; d < 16; ++d) cnt[d * kSortThreads + tid] = (uint32_t)(c >> (4 * d)) & 15u;
+    __syncthreads();
+    // exclusive scan of cnt in index order: thread t takes entries [16t, 16t + 16)
+    uint32_t v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 x = *reinterpret_cast<const uint4*>(&cnt[16 * tid + 4 * q]);
+      v[4 * q] = x.x;
+      v[4 * q + 1] = x.y;
+      v[4 * q + 2] = x.z;
+      v[4 * q + 3] = x.w;
+    }
+    uint32_t tot = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t x = v[j];
+      v[j] = tot;
+      tot += x;
+    }
+    uint32_t inc = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    uint32_t base = inc - tot;
+#pragma unroll
+    for (int q = 0; q < kSortWaves; q += 4) {   // + the totals of the lower waves
+      const uint4 x = *reinterpret_cast<const uint4*>(&wsum[q]);
+      base += (q < wave ? x.x : 0u) + (q + 1 < wave ? x.y : 0u) + (q + 2 < wave ? x.z : 0u) + (q + 3 < wave ? x.w : 0u);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(&cnt[16 * tid + 4 * q]) =
+          uint4{base + v[4 * q], base + v[4 * q + 1], base + v[4 * q + 2], base + v[4 * q + 3]};
+    __syncthreads();
+    uint32_t pos[kLdsSortE];
+#pragma unroll
+    for (int e = 0; e < kLdsSortE; ++e) pos[e] = cnt[(int)((w[e] >> shift) & 15u) * kSortThreads + tid] + rk[e];
+#pragma unroll
+    for (int e = 0; e < kLdsSortE; ++e)
+      if (e < own) buf[pos[e]] = w[e];
+    __syncthreads();
+    if (p + 1 < passes) {
+#pragma unroll
+      for (int e = 0; e < kLdsSortE; ++e) w[e] = buf[min(first + e, n - 1)];
+    }
+  }
+  const uint32_t imask = (1u << ib) - 1u;
+#pragma unroll
+  for (int q = 0; q < kLdsSortE; ++q) {
+    const int j = tid + q * kSortThreads;
+    if (j < n) {
+      const uint32_t x = buf[j], k = x >> ib;
+      keys[j] = k;
+      vals[j] = x & imask;
+      if (k < (uint32_t)vr && (j == 0 || (buf[j - 1] >> ib) != k)) seg[k] = j;
+    }
+  }
+}
+
 // d_emb[v][chunk] = sum over the sorted rows of key v, ascending row order,
 // of d_out[row][chunk] (zeros for rows no id points to).
 template <typename T>
@@ -135,8 +253,9 @@ __global__ __launch_bounds__(256) void embed_grad_kernel(const T* __restrict__ d
   float acc[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) acc[e] = 0.f;
+  // seg[v] counts only where it is the first position of key v (stale entries fail the test)
   const int s = seg[v];
-  if (s >= 0) {
+  if (s >= 0 && s < n && keys[s] == (uint32_t)v && (s == 0 || keys[s - 1] != (uint32_t)v)) {
     for (int i = s; i < n && keys[i] == (uint32_t)v; ++i) {
       Vec16<T> x;
       x.raw = ld16(d_out + (int64_t)vals[i] * cpr * V + j * V);
@@ -149,10 +268,16 @@ __global__ __launch_bounds__(256) void embed_grad_kernel(const T* __restrict__ d
   for (int e = 0; e < V; e += 4) *reinterpret_cast<f32x4*>(o + e) = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
 }
 
-int sort_passes(int vr) {
+int key_bits(int vr) {
   int bits = 0;
   while ((1ll << bits) <= vr) ++bits;   // keys go up to vr (the out-of-range marker)
-  return (bits + 7) / 8;
+  return bits;
+}
+
+int index_bits(int n) {
+  int bits = 0;
+  while ((1ll << bits) < n) ++bits;
+  return bits;
 }
 
 }  // namespace
@@ -186,11 +311,18 @@ hipError_t launch_embedding_bwd(int dtype, const int32_t* tokens, const void* d_
   uint32_t* k1 = va + rows;
   uint32_t* vb = k1 + rows;
   int32_t* seg = reinterpret_cast<int32_t*>(vb + rows);
-  const int passes = sort_passes(vr);
-  uint32_t* keys = (passes & 1) ? k1 : k0;
-  uint32_t* vals = (passes & 1) ? vb : va;
+  const int kb = key_bits(vr), ib = index_bits(n);
+  const bool in_lds = n <= kLdsSortMax && ib + kb <= 32;
+  const int passes = (kb + 7) / 8;
+  uint32_t* keys = (!in_lds && (passes & 1)) ? k1 : k0;
+  uint32_t* vals = (!in_lds && (passes & 1)) ? vb : va;
   hipError_t e;
-  {
+  if (in_lds) {
+    TraceScope trace(K_EMB_SORT, s, (double)rows * 12.0 + (double)vr * 4.0);
+    hipLaunchKernelGGL(embed_sort_lds_kernel, dim3(1), dim3(kSortThreads), 0, s, tokens, n, v0, vr, ib, (kb + 3) / 4,
+                       keys, vals, seg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
     TraceScope trace(K_EMB_SORT, s, (double)rows * 16.0 * passes);
     const int64_t m = std::max<int64_t>(rows, vr);
     hipLaunchKernelGGL(embed_keys_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, tokens, n, v0, vr, k0,

@@ -1,6 +1,11 @@
 """Parity of the vocabulary-parallel input embedding (guide page section 3.3)
 through the C ABI against the oracle: the rank's masked lookup exactly, the
-scatter-add gradient within the fp32 tolerance, bitwise repeatable (GPU)."""
+scatter-add gradient within the fp32 tolerance, bitwise repeatable (GPU).
+The gradient's documented summation order (each vocabulary row adds its
+gradient rows in ascending row order, in fp32) is checked bit for bit
+against that sum done row by row in numpy, which fails if the sort behind it
+is not stable. The cases cover the one-workgroup in-LDS sort (up to 8192
+rows) and the multi-pass sort beyond it."""
 import numpy as np
 import pytest
 import torch
@@ -21,7 +26,26 @@ CASES = [
     (synth.CONFIGS["gpt2_355m_t1"], [0], 0),
     (synth.CONFIGS["gpt2_355m_t1"], [0], 40),
     (synth.CONFIGS["gpt_8p3b_t8"], [0, 7], 0),
+    # 8000 rows, 8 per thread of the in-LDS sort, two ids only: long runs of equal keys
+    (synth.tiny_config("bf16", hidden=128, heads=2, head_dim=64, ffn=256, tp=2, seq=1000, micro_batch=8, vocab=4096,
+                       index=73, name="small_bf16_8000_rows_skewed"), [0, 1], 2),
+    # 9216 rows: beyond the in-LDS sort
+    (synth.tiny_config("bf16", hidden=128, heads=2, head_dim=64, ffn=256, tp=2, seq=1024, micro_batch=9, vocab=4096,
+                       index=74, name="small_bf16_9216_rows"), [0, 1], 0),
+    (synth.tiny_config("bf16", hidden=128, heads=2, head_dim=64, ffn=256, tp=2, seq=1024, micro_batch=9, vocab=4096,
+                       index=75, name="small_bf16_9216_rows_skewed"), [0, 1], 5),
+    (synth.tiny_config("f32", hidden=64, heads=1, head_dim=64, ffn=64, tp=1, seq=1, micro_batch=1, vocab=16,
+                       index=76, name="one_row"), [0], 0),
 ]
+
+
+def _ascending_sum(tok, dout, v0, vr):
+    """fp32 sum of each vocabulary row's gradient rows, in ascending row order."""
+    acc = np.zeros((vr, dout.shape[1]), np.float32)
+    for i, t in enumerate(tok):
+        if v0 <= t < v0 + vr:
+            acc[t - v0] += dout[i]
+    return acc
 
 
 def _dev(a, dtype):
@@ -61,6 +85,8 @@ def test_embedding(cfg, ranks, skew):
         rep = O.compare.compare_tensor(got_g, want_g, "f32")
         print(cfg.name, r, rep)
         assert rep["ok"], rep
+        stored = synth.round_to_bf16(dout) if cfg.dtype == "bf16" else np.asarray(dout, np.float32)
+        assert np.array_equal(got_g, _ascending_sum(tok, stored, r * cfg.vocab_r, cfg.vocab_r))
         parts.append(got_p)
         # deterministic: a second run is bitwise equal
         got_p2, got_g2 = _run(cfg, r, tok, emb, dout)
