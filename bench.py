@@ -223,6 +223,7 @@ def kernel_family(name: str) -> str:
              ("partial_sum", "partial_sum"), ("xent_stats", "xent_stats"), ("xent_finish", "xent_finish"),
              ("xent_dlogits", "xent_dlogits"), ("xent_merge", "xent_merge"), ("embed_fwd", "embedding_fwd"),
              ("embed_grad", "embedding_bwd"), ("embed_keys", "embedding_sort"), ("radix_sort", "embedding_sort"),
+             ("embed_sort", "embedding_sort"),
              ("embed_segments", "embedding_sort")]
     for key, fam in table:
         if key in name:

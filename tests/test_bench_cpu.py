@@ -54,6 +54,8 @@ def test_more_than_one_gpu_is_refused():
      "attn_bwd_dkdv"),
     ("_ZN3tpl12_GLOBAL__N_119xent_dlogits_kernelIDF16bEEvPT_ilPKilPKhPKfS9_f", "xent_dlogits"),
     ("_ZN3tpl12_GLOBAL__N_118ln_fwd_wide_kernelIDF16bLi8EEEvPKT_S4_S4_PS2_PfS6_if", "layernorm_fwd"),
+    ("tpl::(anonymous namespace)::embed_sort_lds_kernel(int const*, int, long, int, int, int, unsigned int*, unsig",
+     "embedding_sort"),
 ])
 def test_kernel_family(kernel, family):
     assert bench.kernel_family(kernel) == family
