@@ -508,14 +508,18 @@ __global__ __launch_bounds__(256) void partial_sum_kernel(PartPtrs parts, int n,
   const int col = (int)(i % (cols / V)) * V;
   const int64_t off = row * cols + col;
   // every load is issued before the first add (n <= 16 partials), then the
-  // values are added in the fixed order residual, bias, partials 0..n-1
+  // values are added in the fixed order residual, bias, partials 0..n-1. The
+  // partials are read once, with the non-temporal hint: eight partials of
+  // 4096 x 3072 took 243 -> 230 us a step so, of 2048 x 12288 527 -> 445 us;
+  // the hint on the store changed nothing.
   const u32x4 zero = {0u, 0u, 0u, 0u};
   const u32x4 rres = residual ? ld16(residual + off) : zero;
   const u32x4 rbias = bias ? ld16(bias + col) : zero;
   u32x4 raw[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k)
-    if (k < n) raw[k] = ld16(static_cast<const T*>(parts.p[k]) + off);
+    if (k < n)
+      raw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const T*>(parts.p[k]) + off));
   float acc[V], t[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) acc[e] = 0.f;
