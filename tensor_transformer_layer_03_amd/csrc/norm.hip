@@ -496,52 +496,69 @@ __global__ __launch_bounds__(1024) void colsum_final_kernel(const float* __restr
 // ------------------------------------------------------------------ partial sum
 struct PartPtrs { const void* p[16]; };
 
-template <typename T>
-__global__ __launch_bounds__(256) void partial_sum_kernel(PartPtrs parts, int n, const T* __restrict__ bias,
+// The partial count NP is a template argument (one instantiation per count,
+// 1..16), so a thread's loads occupy 4 NP registers per chunk instead of the
+// 64 of a runtime count; each thread takes U chunks, 256 apart. bf16 takes
+// U = 2: with eight partials of 4096 x 3072 a step's sums went 230 -> 215 us
+// (447 -> 430 us at 2048 x 12288, four of 8192 x 2560 205 -> 193 us); U = 4
+// was slower than 2 on all three.
+template <typename T, int NP, int U>
+__global__ __launch_bounds__(256) void partial_sum_kernel(PartPtrs parts, const T* __restrict__ bias,
                                                           const T* __restrict__ residual, T* out,
                                                           int64_t rows, int cols) {
   constexpr int V = Vec16<T>::N;
-  const int64_t nvec = rows * (cols / V);
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= nvec) return;
-  const int64_t row = i / (cols / V);
-  const int col = (int)(i % (cols / V)) * V;
-  const int64_t off = row * cols + col;
-  // every load is issued before the first add (n <= 16 partials), then the
-  // values are added in the fixed order residual, bias, partials 0..n-1. The
-  // partials are read once, with the non-temporal hint: eight partials of
-  // 4096 x 3072 took 243 -> 230 us a step so, of 2048 x 12288 527 -> 445 us;
-  // the hint on the store changed nothing.
+  const int cpr = cols / V;
+  const int64_t nvec = rows * cpr;
+  const int64_t i0 = (int64_t)blockIdx.x * (256 * U) + threadIdx.x;
+  // every load is issued before the first add, then the values are added in
+  // the fixed order residual, bias, partials 0..NP-1. The partials are read
+  // once, with the non-temporal hint: eight partials of 4096 x 3072 took
+  // 243 -> 230 us a step so, of 2048 x 12288 527 -> 445 us; the hint on the
+  // store changed nothing.
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  const u32x4 rres = residual ? ld16(residual + off) : zero;
-  const u32x4 rbias = bias ? ld16(bias + col) : zero;
-  u32x4 raw[16];
+  u32x4 rres[U], rbias[U], raw[U][NP];
+  int64_t off[U];
+  int col[U];
 #pragma unroll
-  for (int k = 0; k < 16; ++k)
-    if (k < n)
-      raw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const T*>(parts.p[k]) + off));
-  float acc[V], t[V];
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = i0 + 256 * u;
+    const int64_t row = i / cpr;
+    col[u] = (int)(i - row * cpr) * V;
+    off[u] = row * cols + col[u];
+    rres[u] = rbias[u] = zero;
+    if (i < nvec) {
+      if (residual) rres[u] = ld16(residual + off[u]);
+      if (bias) rbias[u] = ld16(bias + col[u]);
 #pragma unroll
-  for (int e = 0; e < V; ++e) acc[e] = 0.f;
-  if (residual) {
-    unpack<T>(rres, t);
-#pragma unroll
-    for (int e = 0; e < V; ++e) acc[e] += t[e];
+      for (int k = 0; k < NP; ++k)
+        raw[u][k] =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const T*>(parts.p[k]) + off[u]));
+    }
   }
-  if (bias) {
-    unpack<T>(rbias, t);
 #pragma unroll
-    for (int e = 0; e < V; ++e) acc[e] += t[e];
-  }
+  for (int u = 0; u < U; ++u) {
+    if (i0 + 256 * u >= nvec) break;
+    float acc[V], t[V];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    if (k < n) {
-      unpack<T>(raw[k], t);
+    for (int e = 0; e < V; ++e) acc[e] = 0.f;
+    if (residual) {
+      unpack<T>(rres[u], t);
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] += t[e];
     }
+    if (bias) {
+      unpack<T>(rbias[u], t);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += t[e];
+    }
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      unpack<T>(raw[u][k], t);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += t[e];
+    }
+    st16(out + off[u], pack<T>(acc));
   }
-  st16(out + off, pack<T>(acc));
 }
 
 template <typename T, int MAXC>
@@ -725,21 +742,34 @@ hipError_t launch_colsum_final(const float* ws, int64_t nchunks, int cols, float
   return hipGetLastError();
 }
 
+template <typename T, int U>
+hipError_t launch_partial_sum_t(const PartPtrs& pp, int n, const void* bias, const void* residual, void* out,
+                                int64_t rows, int cols, hipStream_t s) {
+  const int64_t nvec = rows * (cols / Vec16<T>::N);
+  const dim3 grid((unsigned)((nvec + 256 * U - 1) / (256 * U)));
+  const T* b = static_cast<const T*>(bias);
+  const T* r = static_cast<const T*>(residual);
+  T* o = static_cast<T*>(out);
+  switch (n) {
+#define TPL_PSUM_CASE(NP) \
+    case NP: hipLaunchKernelGGL((partial_sum_kernel<T, NP, U>), grid, dim3(256), 0, s, pp, b, r, o, rows, cols); break;
+    TPL_PSUM_CASE(1) TPL_PSUM_CASE(2) TPL_PSUM_CASE(3) TPL_PSUM_CASE(4) TPL_PSUM_CASE(5) TPL_PSUM_CASE(6)
+    TPL_PSUM_CASE(7) TPL_PSUM_CASE(8) TPL_PSUM_CASE(9) TPL_PSUM_CASE(10) TPL_PSUM_CASE(11) TPL_PSUM_CASE(12)
+    TPL_PSUM_CASE(13) TPL_PSUM_CASE(14) TPL_PSUM_CASE(15) TPL_PSUM_CASE(16)
+#undef TPL_PSUM_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_partial_sum(int dtype, const void* const* parts, int n, const void* bias, const void* residual,
                               void* out, int64_t rows, int cols, hipStream_t s) {
   TraceScope trace(K_PARTIAL_SUM, s, (double)rows * cols * (n + 1 + (residual ? 1 : 0)) * dtype_size(dtype));
+  if (n < 1 || n > 16) return hipErrorInvalidValue;
   PartPtrs pp;
   for (int i = 0; i < 16; ++i) pp.p[i] = i < n ? parts[i] : nullptr;
-  const int v = dtype == DT_BF16 ? 8 : 4;
-  const int64_t nvec = rows * (cols / v);
-  const dim3 grid((unsigned)((nvec + 255) / 256));
-  if (dtype == DT_BF16)
-    hipLaunchKernelGGL(partial_sum_kernel<bf16>, grid, dim3(256), 0, s, pp, n, static_cast<const bf16*>(bias),
-                       static_cast<const bf16*>(residual), static_cast<bf16*>(out), rows, cols);
-  else
-    hipLaunchKernelGGL(partial_sum_kernel<float>, grid, dim3(256), 0, s, pp, n, static_cast<const float*>(bias),
-                       static_cast<const float*>(residual), static_cast<float*>(out), rows, cols);
-  return hipGetLastError();
+  if (dtype == DT_BF16) return launch_partial_sum_t<bf16, 2>(pp, n, bias, residual, out, rows, cols, s);
+  return launch_partial_sum_t<float, 1>(pp, n, bias, residual, out, rows, cols, s);
 }
 
 }  // namespace tpl
