@@ -2,8 +2,9 @@
 row-parallel bias and the residual, against the oracle within the dtype's
 tolerance and bit for bit against the documented order (fp32 accumulation
 of residual, bias, partials 0..n-1, rounded once to the storage type), for
-every partial count the kernel is instantiated for, ragged row counts (a
-thread's second chunk past the end) and an output that aliases the residual."""
+partial counts from 1 to 16 (the kernel has one instantiation per count),
+ragged row counts (a thread's second chunk past the end) and an output that
+aliases the residual."""
 import numpy as np
 import pytest
 import torch
