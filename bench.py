@@ -293,7 +293,18 @@ def embedding_bench(cfg, steps, torch, B):
             "bound": "hbm", "peak_gbs": 8000.0}
 
 
-def summarize_profiles(d: str, workload: str):
+DEFAULT_WORKLOAD = "gpt2_355m_t1"
+
+
+def trace_cmd(workload: str) -> str:
+    """The kernel-trace command of PROFILE_CMDS for a workload."""
+    cmd = PROFILE_CMDS["trace"]
+    if workload == DEFAULT_WORKLOAD:
+        return cmd
+    return cmd.replace("bench.py --steps", f"bench.py --config {workload} --steps")
+
+
+def summarize_profiles(d: str, workload: str, trace_only: bool = False):
     import csv
     import collections
     prof = os.path.join(ROOT, "profiles")
@@ -307,7 +318,7 @@ def summarize_profiles(d: str, workload: str):
         fam[f][1] += float(r["TotalDurationNs"])
     total = sum(v[1] for v in fam.values())
     lines = [f"# Kernel time, {workload} (rocprofv3 --kernel-trace --stats)", "",
-             "Command (repo root = <repo>, output dir = <out>):", "", "    " + PROFILE_CMDS["trace"], "",
+             "Command (repo root = <repo>, output dir = <out>):", "", "    " + trace_cmd(workload), "",
              "Every launch of the run (warm-up, timed and traced steps); all are whole passes, so the mix per",
              "kernel family is the same as in one step. A weight-gradient product's split-K sum is counted",
              "in its launch (gemm_tn), as the library's own launch timing does.", "",
@@ -319,6 +330,8 @@ def summarize_profiles(d: str, workload: str):
         lines.append(f"| {r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.3f} |")
     open(os.path.join(prof, f"kernel_stats_{workload}.md"), "w").write("\n".join(lines) + "\n")
+    if trace_only:
+        return
     # HBM bytes: FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a plain copy of known size
     copy_bytes = 1024 * (1 << 20)
     per = {}
@@ -388,7 +401,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="gpt2_355m_t1")
+    ap.add_argument("--config", default=DEFAULT_WORKLOAD)
     ap.add_argument("--trace-steps", type=int, default=3)
     ap.add_argument("--cpu-seqs", type=int, default=-1,
                     help="sequences in the CPU-baseline sample (-1 = the whole micro-batch, 0 = skip)")
@@ -397,10 +410,12 @@ def main():
                     help="skip the extra timing of the layer fwd+bwd without the loss")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 CSV output under DIR and exit")
+    ap.add_argument("--trace-only", action="store_true",
+                    help="with --summarize-profiles: the kernel-trace summary only (no counter passes)")
     args = ap.parse_args()
 
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles, args.config)
+        summarize_profiles(args.summarize_profiles, args.config, args.trace_only)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -59,3 +59,9 @@ def test_more_than_one_gpu_is_refused():
 ])
 def test_kernel_family(kernel, family):
     assert bench.kernel_family(kernel) == family
+
+
+def test_trace_command_names_the_workload():
+    assert "--config" not in bench.trace_cmd(bench.DEFAULT_WORKLOAD)
+    cmd = bench.trace_cmd("gpt_175b_t8")
+    assert "bench.py --config gpt_175b_t8 --steps 5" in cmd and cmd.startswith("cd /tmp && rocprofv3 --kernel-trace")
