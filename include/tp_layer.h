@@ -31,7 +31,10 @@
  *     frees device memory, never keeps a pointer after a call returns and never
  *     synchronises: all work is enqueued on `stream` (a hipStream_t; NULL = the
  *     default stream). Calls are reentrant; buffers passed to concurrent calls
- *     must not overlap.
+ *     must not overlap. The profiling helpers tpl_trace_* are the one
+ *     exception: while enabled they keep process-wide state (an event pool
+ *     and its records), create HIP events, and tpl_trace_read synchronises
+ *     on the recorded events; the computation calls never depend on them.
  *   - Errors: arguments are validated on the host before anything is
  *     launched; a failed check returns TPL_ERR_INVALID_ARG (bad value, null or
  *     misaligned pointer) or TPL_ERR_UNSUPPORTED (valid but not implemented,
@@ -140,7 +143,16 @@ tpl_status shard_partial_sum(const tpl_desc* desc, const void* const* partials, 
                              int32_t cols, void* stream);
 
 /* Backward of one block on this rank, in two phases around the all-reduce of
- * the gradient w.r.t. the block's LayerNorm output.
+ * the gradient w.r.t. the block's LayerNorm output. Defining passages:
+ * podcast page "Megatron-LM's parallelism", Outline (two all-reduces per
+ * module, four per layer forward+backward: in the backward each block's
+ * input gradient is all-reduced once; LayerNorm, dropout and the residual
+ * are duplicated on every rank, so their backward runs replicated after the
+ * all-reduce); guide page "From Transformer splitting to communication
+ * optimisation", section 3.1 (the MLP's column-parallel first layer and
+ * row-parallel second layer, so GeLU's gradient is local to the rank's
+ * columns) and section 3.2 (QKV split by heads, output projection split by
+ * rows).
  *   TPL_BWD_SHARD: from dy ([N][h], gradient of the block output) and `saved`,
  *     writes d_ln_partial [N][h] (this rank's partial gradient w.r.t. the LN
  *     output) and grads->d_w_in, d_b_in, d_w_out.
@@ -198,20 +210,6 @@ tpl_status vocab_parallel_xent_fwd(const tpl_desc* desc, tpl_xent_phase phase,
                                    const float* const* all_stats, float* lse, float* loss_rows,
                                    float* loss, void* stream);
 
-/* Vocabulary-parallel input embedding (guide page 3.3: the input layer is
- * split along the vocabulary and the ranks' outputs summed by an all-reduce).
- *   fwd: x_partial [N][h] (storage dtype) row n = E_r[tokens[n] - rank*V_r] if
- *     the id lies in this rank's range [rank*V_r, (rank+1)*V_r), else zeros.
- *     shard_partial_sum over the ranks' partials (the all-reduce) gives the
- *     lookup E[tokens[n]].
- *   bwd: from d_out [N][h] (storage dtype; the gradient of the summed output,
- *     the same on every rank), d_emb_in [V_r][h] fp32 (overwritten) row v =
- *     sum of d_out[n] over the rows whose id is rank*V_r + v, added in
- *     ascending n (a stable sort of the ids, no float atomics: deterministic);
- *     rows no id points to are zero. No communication.
- * tokens: [N] int32 global ids (ids outside [0, V) contribute nothing);
- * emb_in: E_r [V_r][h] storage dtype; workspace: device scratch of
- * vocab_parallel_embedding_ws_bytes(desc) bytes, overwritten. */
 /* Loss rows of a masked loss (podcast page, Outline: the large-BERT variant;
  * its masked-token loss is taken on a fraction of the positions). The loss
  * needs logits, dlogits, dH and dE only for those rows, so a caller that knows
@@ -231,13 +229,33 @@ tpl_status tpl_rows_gather(const void* src, int64_t n_src, const int32_t* rows, 
 tpl_status tpl_rows_expand(const void* src, int64_t n_src, const int32_t* pos, int64_t n_dst, int64_t row_bytes,
                            void* dst, void* stream);
 
+/* Vocabulary-parallel input embedding (guide page 3.3: the input layer is
+ * split along the vocabulary and the ranks' outputs summed by an all-reduce).
+ *   fwd: x_partial [N][h] (storage dtype) row n = E_r[tokens[n] - rank*V_r] if
+ *     the id lies in this rank's range [rank*V_r, (rank+1)*V_r), else zeros.
+ *     shard_partial_sum over the ranks' partials (the all-reduce) gives the
+ *     lookup E[tokens[n]].
+ *   bwd: from d_out [N][h] (storage dtype; the gradient of the summed output,
+ *     the same on every rank), d_emb_in [V_r][h] fp32 (overwritten) row v =
+ *     sum of d_out[n] over the rows whose id is rank*V_r + v, added in
+ *     ascending n (a stable sort of the ids, no float atomics: deterministic);
+ *     rows no id points to are zero. No communication.
+ * tokens: [N] int32 global ids (ids outside [0, V) contribute nothing);
+ * emb_in: E_r [V_r][h] storage dtype; workspace: device scratch of
+ * vocab_parallel_embedding_ws_bytes(desc) bytes, overwritten. */
 size_t vocab_parallel_embedding_ws_bytes(const tpl_desc* desc);
 tpl_status vocab_parallel_embedding_fwd(const tpl_desc* desc, const int32_t* tokens, const void* emb_in,
                                         void* x_partial, void* stream);
 tpl_status vocab_parallel_embedding_bwd(const tpl_desc* desc, const int32_t* tokens, const void* d_out,
                                         float* d_emb_in, void* workspace, void* stream);
 
-/* Vocabulary-parallel cross-entropy backward for this rank.
+/* Vocabulary-parallel cross-entropy backward for this rank (guide page
+ * "From Transformer splitting to communication optimisation", section 3.3:
+ * the output layer split along the vocabulary with the gather deferred into
+ * the cross-entropy, so each rank forms the gradient of its own logits from
+ * the exchanged row statistics and needs one all-reduce of its hidden-state
+ * gradient; podcast page, Outline: output embedding split along the
+ * vocabulary, loss fused in).
  *   dlogits = g_n (exp(logits - lse_n) - [j == targets[n] - rank*V_r]) with
  *   g_n = dloss * mask[n] / loss[1], written IN PLACE over `logits`;
  *   d_hidden_partial = dlogits E_r ([N][h], storage dtype; summed over ranks

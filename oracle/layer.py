@@ -179,10 +179,13 @@ def attn_block_bwd_shard(dy, p, cache):
 
 
 def mlp_block_fwd(h1, p, eps):
-    """MLP block of one rank: pre-LN, column-parallel fc1 + GeLU, row-parallel
-    fc2 -> partial (guide page section 3.1: fc1 split by columns so GeLU needs
-    no exchange, fc2 split by rows and fed directly; its ParallelMLP sketch
-    composes fc2(gelu(fc1(x))) with a 4x ffn width)."""
+    """MLP block of one rank: pre-LN, then the column-parallel first linear
+    layer with its bias, GeLU applied to this rank's columns, then the
+    row-parallel second linear layer on those columns -> partial (guide page
+    "From Transformer splitting to communication optimisation", section 3.1:
+    the first layer is split by columns so GeLU needs no exchange, the second
+    by rows so it consumes the local columns directly; the ffn is four times
+    the hidden width there)."""
     z, mu, rstd, xhat = layernorm_fwd(h1, p["ln2_g"], p["ln2_b"], eps)
     u = linear(z, p["w1"], p["b1"])
     a = gelu(u)

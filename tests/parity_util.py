@@ -2,6 +2,8 @@
 pass through the C ABI, the oracle's reference of the same pass."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 import oracle as O
@@ -31,11 +33,33 @@ def run_gpu(cfg, rep, shards, peers, peer_stats, repeats=1):
     return res, st
 
 
-def run_oracle(cfg, rep, shards, peers, peer_stats):
+def run_gpu_recompute(cfg, rep, shards, peers, peer_stats):
+    """One pass whose layer backward recomputes each block's forward stash
+    (activation recomputation): after the forward and the loss, every stash
+    is overwritten, so only the recomputed values can make the backward
+    right."""
+    import torch
+    from tensor_transformer_layer_03_amd.step import LayerStep
+    st = LayerStep(cfg, rep, {r: synth.device_shard(cfg, s) for r, s in shards.items()}, peers, peer_stats,
+                   recompute=True)
+    st.forward()
+    st.xent_forward()
+    st.xent_backward()
+    st.poison_saved()
+    st.backward()
+    torch.cuda.synchronize()
+    res = st.results()
+    res["loss"] = res["loss"][:2]
+    return res, st
+
+
+def run_oracle(cfg, rep, shards, peers, peer_stats, mags=None):
+    """The oracle's pass; with a dict `mags`, also the magnitudes of the
+    terms behind every output (the parity gate's rounding allowance)."""
     prs = {r: synth.oracle_params(cfg, [s], rep) for r, s in shards.items()}
     return O.step_reference(prs, rep.x, rep.dout, rep.targets, rep.mask, seq=cfg.seq, causal=cfg.causal,
                             eps=cfg.ln_eps, tp=cfg.tp, vocab_r=cfg.vocab_r, peers=peers, peer_stats=peer_stats,
-                            use_mask=cfg.mask_rows is not None)
+                            use_mask=cfg.mask_rows is not None, mags=mags)
 
 
 def loss_rows_only(ref: dict, mask) -> dict:
@@ -51,14 +75,27 @@ def loss_rows_only(ref: dict, mask) -> dict:
     return out
 
 
-def check_case(cfg, ranks=None, verbose=True):
+def check_case(cfg, ranks=None, verbose=True, recompute=False):
+    """One pass on the GPU against the oracle under the gate of
+    oracle/compare.py (every element in band); recompute=True runs the
+    activation-recomputing backward on overwritten stashes."""
     rep, shards, peers, peer_stats = build_case(cfg, ranks)
-    got, st = run_gpu(cfg, rep, shards, peers, peer_stats)
-    ref = run_oracle(cfg, rep, shards, peers, peer_stats)
+    run = run_gpu_recompute if recompute else run_gpu
+    got, st = run(cfg, rep, shards, peers, peer_stats)
+    mags = {}
+    ref = run_oracle(cfg, rep, shards, peers, peer_stats, mags)
     if cfg.mask_rows is not None:
         ref = loss_rows_only(ref, rep.mask)
-    report = O.compare.compare_all(got, ref, cfg.dtype)
+        mags = loss_rows_only(mags, rep.mask)
+    report = O.compare.compare_all(got, ref, cfg.dtype, mags)
+    out_dir = os.environ.get("TPL_PARITY_REPORT_DIR")
+    if out_dir:   # per-tensor report of this case (out-of-band count, worst ratio, errors)
+        os.makedirs(out_dir, exist_ok=True)
+        tag = f"{cfg.name}_r{'-'.join(map(str, sorted(shards)))}{'_recompute' if recompute else ''}"
+        with open(os.path.join(out_dir, tag + ".txt"), "w") as f:
+            f.write(f"{cfg.name} ranks={sorted(shards)} dtype={cfg.dtype}{' recompute' if recompute else ''}\n")
+            f.write(O.compare.format_report(report) + "\n")
     if verbose:
-        print(f"\n== {cfg.name} ranks={sorted(shards)} dtype={cfg.dtype}")
+        print(f"\n== {cfg.name} ranks={sorted(shards)} dtype={cfg.dtype}{' recompute' if recompute else ''}")
         print(O.compare.format_report(report), flush=True)
     return report, st
