@@ -7,9 +7,15 @@ fc1+GeLU, fc2, all-reduce stand-in), vocabulary-parallel cross-entropy
 forward and backward, layer backward (both blocks, both phases, and the
 backward all-reduce stand-ins). Inputs are resident in HBM before timing.
 
-Prints ONE JSON line. `value` = algorithmic flops of the step (layer shard
-fwd+bwd, causal attention counted over visible pairs only, plus the loss's
-logits fwd/dgrad/wgrad) / measured step time, in TFLOP/s.
+Prints ONE JSON line. `value` = algorithmic flops of one rank's layer shard
+forward + backward (3 x the forward's contraction flops, causal attention
+over visible query-key pairs only) / the median over the timed steps of the
+time spent in that rank's own layer calls (both blocks' forward, both
+backward phases of both blocks; event pairs around each call). The all-reduce
+stand-ins (which on t GPUs are RCCL all-reduces over xGMI) and the loss are
+timed and reported beside it, not in it. The default workload is the 175B
+rank (the largest single-GPU workload); the other bf16 workloads are measured
+in the same run and reported under `workloads`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
        python bench.py --copy-calibration     (plain copy for PMC byte scaling)
@@ -68,19 +74,85 @@ def time_loop(fn, steps, torch):
     return start.elapsed_time(end) / steps
 
 
-def step_percentiles(fn, steps, torch):
-    """Per-step milliseconds (an event pair per step on the current stream):
-    p10, median, p90."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, b in evs:
-        a.record()
-        fn()
-        b.record()
-    torch.cuda.synchronize()
-    t = sorted(a.elapsed_time(b) for a, b in evs)
+def quantiles(xs):
+    t = sorted(xs)
     q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
-    return {"p10": round(q(0.1), 4), "median": round(q(0.5), 4), "p90": round(q(0.9), 4), "steps": steps}
+    return {"p10": round(q(0.1), 4), "median": round(q(0.5), 4), "p90": round(q(0.9), 4)}
+
+
+class CallTimer:
+    """LayerStep hook: an event pair on the current stream around every
+    library call of a pass, labelled with the call's kind ("layer", "sum",
+    "loss") and the step index."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.step = 0
+        self.recs = []
+
+    def __call__(self, kind, thunk):
+        E = self.torch.cuda.Event
+        a, b = E(enable_timing=True), E(enable_timing=True)
+        a.record()
+        r = thunk()
+        b.record()
+        self.recs.append((self.step, kind, a, b))
+        return r
+
+    def per_step(self, steps):
+        """{kind: [ms of that kind's calls in step i for i < steps]} (after a sync)."""
+        out = {}
+        for i, kind, a, b in self.recs:
+            out.setdefault(kind, [0.0] * steps)[i] += a.elapsed_time(b)
+        return out
+
+
+def measure(st, steps, warmup, torch):
+    """Warm-up, then `steps` timed passes between two synchronisations. Each
+    pass is bracketed by an event pair and each library call inside it by its
+    own (CallTimer). Returns the mean step time over the timed region and the
+    per-step times of the whole pass and of each call kind."""
+    for _ in range(warmup):
+        st.step()
+    E = torch.cuda.Event
+    timer = CallTimer(torch)
+    st.hook = timer
+    pairs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(steps)]
+    t0, t1 = E(enable_timing=True), E(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i, (a, b) in enumerate(pairs):
+        timer.step = i
+        a.record()
+        st.step()
+        b.record()
+    t1.record()
+    torch.cuda.synchronize()
+    st.hook = None
+    kinds = timer.per_step(steps)
+    return {"mean_step_ms": t0.elapsed_time(t1) / steps, "step": [a.elapsed_time(b) for a, b in pairs],
+            "layer": kinds.get("layer", [0.0] * steps), "sum": kinds.get("sum", [0.0] * steps),
+            "loss": kinds.get("loss", [0.0] * steps)}
+
+
+def summary(cfg, n_ranks, m, peak):
+    """Throughput figures of one workload from measure()'s per-step times."""
+    fl = step_flops(cfg, n_ranks)
+    lq, sq, xq, tq = (quantiles(m[k]) for k in ("layer", "sum", "loss", "step"))
+    tf = lambda f, ms: round(f / (ms / 1e3) / 1e12, 2)
+    return {
+        "layer_shard": {"tflops": tf(fl["layer"], lq["median"]),
+                        "pct_of_mfma_peak": round(100 * fl["layer"] / (lq["median"] / 1e3) / 1e12 / peak, 2),
+                        "ms": lq, "gflop": round(fl["layer"] / 1e9, 1),
+                        "note": "the rank's own layer calls (fwd ATTN, fwd MLP, bwd MLP shard + replicated, "
+                                "bwd ATTN shard + replicated), median over steps"},
+        "standin_sums": {"ms": sq, "calls_per_step": 5,
+                         "note": "shard_partial_sum, the all-reduce stand-in (4 per layer + the loss gradient's)"},
+        "loss": {"tflops": tf(fl["xent"], xq["median"]), "ms": xq, "gflop": round(fl["xent"] / 1e9, 1),
+                 "note": "vocabulary-parallel cross-entropy forward (local + finish) and backward"},
+        "step": {"tflops": tf(fl["total"], tq["median"]), "ms": tq,
+                 "note": "whole pass: layer, loss and the stand-in sums"},
+    }
 
 
 def traced_kernels(st, steps, B, dtype):
@@ -97,21 +169,6 @@ def traced_kernels(st, steps, B, dtype):
         c, t, w = agg.get(name, (0, 0.0, 0.0))
         agg[name] = (c + 1, t + ms, w + work)
     return agg
-
-
-def standin_sum_ms(st, passes, B):
-    """Event-timed milliseconds per layer pass (forward + backward) spent in
-    the all-reduce stand-in (shard_partial_sum), which on t GPUs would be an
-    RCCL all-reduce over xGMI rather than work of this rank."""
-    import torch
-    B.tpl_trace_enable(4096)
-    for _ in range(passes):
-        st.forward()
-        st.backward()
-    torch.cuda.synchronize()
-    recs = B.tpl_trace_read(4096)
-    B.tpl_trace_enable(0)
-    return sum(ms for name, ms, _ in recs if name == "partial_sum") / passes
 
 
 def roofline(agg, dtype, workload):
@@ -132,12 +189,12 @@ def roofline(agg, dtype, workload):
             "avg_launch_us": round(ms / count * 1e3, 2), "bytes_per_launch": work / count}
 
 
-def cpu_baseline(cfg, seqs: int, repeats: int = 3) -> dict:
+def cpu_baseline(cfg, seqs: int, seq_len: int, repeats: int = 3) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload:
-    `seqs` sequences of the micro-batch (every flop of those rows), median of
+    `seqs` sequences of `seq_len` tokens (the workload's layer, loss and
+    rank split at a shorter length; every flop of that sample), median of
     `repeats` runs."""
     import dataclasses
-    import numpy as np
     import oracle as O
     import synth
     try:
@@ -145,9 +202,11 @@ def cpu_baseline(cfg, seqs: int, repeats: int = 3) -> dict:
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:  # threadpoolctl missing: report the affinity mask
         threads = len(os.sched_getaffinity(0))
-    seqs = min(seqs, cfg.micro_batch)
-    small = dataclasses.replace(cfg, micro_batch=seqs,
-                                mask_rows=None if cfg.mask_rows is None else max(1, cfg.mask_rows * seqs // cfg.micro_batch))
+    seqs = max(1, min(seqs, cfg.micro_batch))
+    seq_len = max(1, min(seq_len, cfg.seq))
+    rows = seqs * seq_len
+    small = dataclasses.replace(cfg, micro_batch=seqs, seq=seq_len,
+                                mask_rows=None if cfg.mask_rows is None else max(1, cfg.mask_rows * rows // cfg.rows))
     ranks = small.ranks()
     rep = synth.replicated_inputs(small)
     shards = {r: synth.rank_shard(small, r) for r in ranks}
@@ -165,8 +224,9 @@ def cpu_baseline(cfg, seqs: int, repeats: int = 3) -> dict:
     dt = sorted(times)[len(times) // 2]
     fl = step_flops(small, len(ranks))["total"]
     return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle pass (numpy fp64) over {seqs} of {cfg.micro_batch} sequences, median of "
-                      f"{repeats} runs ({fl / 1e9:.0f} GFLOP in {dt:.1f} s each)"}
+            "sample": f"oracle pass (numpy fp64: layer shard fwd+bwd and the loss) over {seqs} of "
+                      f"{cfg.micro_batch} sequences at {seq_len} of {cfg.seq} tokens, median of {repeats} runs "
+                      f"({fl / 1e9:.0f} GFLOP in {dt:.1f} s each)"}
 
 
 def copy_calibration(torch, mib=1024, reps=5):
@@ -186,13 +246,15 @@ SOURCES = {"gemm": "gemm.hip", "attn": "attention.hip", "layernorm": "norm.hip",
            "partial": "norm.hip", "xent": "xent.hip", "embedding": "embedding.hip"}
 PROFILE_CMDS = {
     "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_c2 -o c2 -- "
-             "python3 <repo>/bench.py --steps 5 --warmup 2 --cpu-seqs 0 --no-layer-only",
+             "python3 <repo>/bench.py --config <workload> --steps 5 --warmup 2 --cpu-seqs 0 --no-layer-only",
     "pmc": "cd /tmp && rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <out>/pmc_<counter> -o bench "
-           "-- python3 <repo>/bench.py --steps 2 --warmup 1 --cpu-seqs 0 --trace-steps 1 --no-layer-only",
+           "-- python3 <repo>/bench.py --config <workload> --steps 2 --warmup 1 --cpu-seqs 0 --trace-steps 1 "
+           "--no-layer-only",
     "copy": "cd /tmp && rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <out>/pmc_<counter> -o copy "
             "-- python3 <repo>/bench.py --copy-calibration",
     "mfma": "cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES --output-format csv -d <out>/pmc_mfma "
-            "-o bench -- python3 <repo>/bench.py --steps 2 --warmup 1 --cpu-seqs 0 --trace-steps 1 --no-layer-only",
+            "-o bench -- python3 <repo>/bench.py --config <workload> --steps 2 --warmup 1 --cpu-seqs 0 "
+            "--trace-steps 1 --no-layer-only",
 }
 
 
@@ -293,15 +355,18 @@ def embedding_bench(cfg, steps, torch, B):
             "bound": "hbm", "peak_gbs": 8000.0}
 
 
-DEFAULT_WORKLOAD = "gpt2_355m_t1"
+DEFAULT_WORKLOAD = "gpt_175b_t8"
+BF16_WORKLOADS = ["gpt2_355m_t1", "gpt_8p3b_t8", "bert_3p9b_t4", "gpt_175b_t8"]
+
+
+def profile_cmd(kind: str, workload: str) -> str:
+    """A command of PROFILE_CMDS for a workload."""
+    return PROFILE_CMDS[kind].replace("<workload>", workload)
 
 
 def trace_cmd(workload: str) -> str:
     """The kernel-trace command of PROFILE_CMDS for a workload."""
-    cmd = PROFILE_CMDS["trace"]
-    if workload == DEFAULT_WORKLOAD:
-        return cmd
-    return cmd.replace("bench.py --steps", f"bench.py --config {workload} --steps")
+    return profile_cmd("trace", workload)
 
 
 def summarize_profiles(d: str, workload: str, trace_only: bool = False):
@@ -351,10 +416,16 @@ def summarize_profiles(d: str, workload: str, trace_only: bool = False):
                    "write_bytes_per_launch": per["WRITE_SIZE"].get(f, 0.0),
                    "bytes_per_launch": per["FETCH_SIZE"].get(f, 0.0) + per["WRITE_SIZE"].get(f, 0.0),
                    "source_sha256": source_sha(f)} for f in per["FETCH_SIZE"]}
-    json.dump({"workload": workload, "scale": scale, "kernels": traffic},
-              open(os.path.join(prof, "hbm_traffic.json"), "w"), indent=1)
+    path = os.path.join(prof, "hbm_traffic.json")
+    try:
+        doc = json.load(open(path))
+        doc.setdefault("workloads", {})
+    except (OSError, ValueError):
+        doc = {"workloads": {}}
+    doc["workloads"][workload] = {"scale": scale, "kernels": traffic}
+    json.dump(doc, open(path, "w"), indent=1)
     lines = [f"# HBM bytes per launch, {workload} (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
-             "Commands:", "", "    " + PROFILE_CMDS["pmc"], "    " + PROFILE_CMDS["copy"], "",
+             "Commands:", "", "    " + profile_cmd("pmc", workload), "    " + PROFILE_CMDS["copy"], "",
              f"Calibration: a {copy_bytes >> 20} MiB device copy reads and writes {copy_bytes >> 20} MiB; the counters "
              f"read FETCH x{1 / scale['FETCH_SIZE']:.3f}, WRITE x{1 / scale['WRITE_SIZE']:.3f} of that, so bench "
              f"bytes are scaled by {scale['FETCH_SIZE']:.3f} (fetch) and {scale['WRITE_SIZE']:.3f} (write).", "",
@@ -370,7 +441,7 @@ def summarize_profiles(d: str, workload: str, trace_only: bool = False):
             f = kernel_family(r["Kernel_Name"])
             busy[f][0 if r["Counter_Name"] == "SQ_VALU_MFMA_BUSY_CYCLES" else 1] += float(r["Counter_Value"])
         lines = [f"# MFMA busy share per kernel family, {workload} (rocprofv3 --pmc)", "",
-                 "Command:", "", "    " + PROFILE_CMDS["mfma"], "",
+                 "Command:", "", "    " + profile_cmd("mfma", workload), "",
                  "share = SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES), summed over the family's dispatches:",
                  "the fraction of SIMD cycles (4 SIMDs per CU) with the matrix unit busy while the CUs are busy.", "",
                  "| family | MFMA busy share |", "|---|---|"]
@@ -382,16 +453,13 @@ def summarize_profiles(d: str, workload: str, trace_only: bool = False):
 
 
 def measured_traffic(family: str, workload: str):
-    """HBM bytes per launch from the committed counter summary, or None if the
-    counters were taken on another workload or the kernel's source changed
-    since."""
+    """HBM bytes per launch of a kernel family on a workload from the committed
+    counter summaries, or None if no counters were taken on that workload or
+    the kernel's source changed since."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
-        doc = json.load(open(path))
-        rec = doc["kernels"][family]
-    except (OSError, KeyError, ValueError):
-        return None
-    if doc.get("workload") != workload:
+        rec = json.load(open(path))["workloads"][workload]["kernels"][family]
+    except (OSError, KeyError, ValueError, TypeError):
         return None
     return rec["bytes_per_launch"] if rec.get("source_sha256") == source_sha(family) else None
 
@@ -403,11 +471,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_WORKLOAD)
     ap.add_argument("--trace-steps", type=int, default=3)
-    ap.add_argument("--cpu-seqs", type=int, default=-1,
-                    help="sequences in the CPU-baseline sample (-1 = the whole micro-batch, 0 = skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=1,
+                    help="sequences in the CPU-baseline sample (0 = skip)")
+    ap.add_argument("--cpu-seq-len", type=int, default=512,
+                    help="tokens per sequence in the CPU-baseline sample (at most the workload's)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--no-layer-only", dest="layer_only", action="store_false",
-                    help="skip the extra timing of the layer fwd+bwd without the loss")
+    ap.add_argument("--no-layer-only", dest="all_workloads", action="store_false",
+                    help="time the chosen workload only (skip the other bf16 workloads' records)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 CSV output under DIR and exit")
     ap.add_argument("--trace-only", action="store_true",
@@ -435,33 +505,40 @@ def main():
     from tensor_transformer_layer_03_amd import binding as B
 
     cfg = synth.get_config(args.config)
+    peak = PEAK_TFLOPS[cfg.dtype]
     st, ranks = build_step(cfg)
     fl = step_flops(cfg, len(ranks))
-
-    for _ in range(args.warmup):
-        st.step()
-    ms = time_loop(st.step, args.steps, torch)
-    ms_layer = (time_loop(lambda: (st.forward(), st.backward()), max(3, args.steps // 2), torch)
-                if args.layer_only else None)
-    pct = step_percentiles(st.step, args.steps, torch)
-    sums_ms = standin_sum_ms(st, 3, B) if args.layer_only else None
+    m = measure(st, args.steps, args.warmup, torch)
+    head = summary(cfg, len(ranks), m, peak)
     agg = traced_kernels(st, args.trace_steps, B, cfg.dtype)
     loss = float(st.shared["loss"][0].item())
     emb = embedding_bench(cfg, args.steps, torch, B)
     rec = recompute_bench(st, max(3, args.steps // 2), torch)
+    del st
+    torch.cuda.empty_cache()
 
-    value = fl["total"] / (ms / 1e3) / 1e12
-    peak = PEAK_TFLOPS[cfg.dtype]
+    workloads = {}
+    if args.all_workloads:
+        for name in BF16_WORKLOADS:
+            if name == cfg.name:
+                workloads[name] = head
+                continue
+            c2 = synth.get_config(name)
+            s2, r2 = build_step(c2)
+            workloads[name] = summary(c2, len(r2), measure(s2, args.steps, args.warmup, torch), PEAK_TFLOPS[c2.dtype])
+            del s2
+            torch.cuda.empty_cache()
+
+    value = head["layer_shard"]["tflops"]
     kernels = sorted(((k, c, t / args.trace_steps, w) for k, (c, t, w) in agg.items()), key=lambda r: -r[2])
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "step_ms_percentiles": pct,
+        "ms_per_step": round(m["mean_step_ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -474,19 +551,15 @@ def main():
                         f"{'causal' if cfg.causal else 'bidirectional'}",
             "global_batch": cfg.micro_batch, "seq_len": cfg.seq, "parallelism": f"tp{cfg.tp} (one GPU)",
         },
-        "pct_of_mfma_peak": round(100 * value / peak, 2),
+        "pct_of_mfma_peak": head["layer_shard"]["pct_of_mfma_peak"],
+        "value_definition": "layer-shard fwd+bwd flops / median time of the rank's own layer calls "
+                            "(all-reduce stand-ins and the loss excluded; reported below)",
+        "ms_per_step_definition": "mean time of a whole pass (layer, loss, stand-in sums) over the timed steps",
         "flops_per_step": fl,
-        "layer_only": None if ms_layer is None else {
-            "ms": round(ms_layer, 4), "tflops": round(fl["layer"] / (ms_layer / 1e3) / 1e12, 2),
-            "note": "layer fwd+bwd with its 4 all-reduce stand-ins, loss excluded",
-            "excl_standin_sums": {
-                "ms": round(ms_layer - sums_ms, 4),
-                "tflops": round(fl["layer"] / ((ms_layer - sums_ms) / 1e3) / 1e12, 2),
-                "pct_of_mfma_peak": round(100 * fl["layer"] / ((ms_layer - sums_ms) / 1e3) / 1e12 / peak, 2),
-                "note": "the rank's own calls: layer time minus the event-timed shard_partial_sum launches "
-                        "(stand-ins for the all-reduce on t GPUs)"}},
-        "loss": round(loss, 6),
+        **head,
+        "loss_value": round(loss, 6),
         "roofline": roofline(agg, cfg.dtype, cfg.name),
+        "workloads": workloads,
         "embedding": emb,
         "recompute": rec,
         "kernels_per_step": [{"kernel": k, "launches": c // args.trace_steps, "ms": round(t, 4),
@@ -495,7 +568,7 @@ def main():
                              for k, c, t, w in kernels],
     }
     if args.cpu_seqs != 0:
-        out["cpu_baseline"] = cpu_baseline(cfg, cfg.micro_batch if args.cpu_seqs < 0 else args.cpu_seqs)
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seqs, args.cpu_seq_len)
     print(json.dumps(out), flush=True)
 
 

@@ -70,6 +70,11 @@ class LayerStep:
     def __init__(self, cfg, rep, shards: dict, peers=(), peer_stats=(), device="cuda", recompute=False):
         self.cfg = cfg
         self.recompute = recompute   # backward rebuilds each block's forward stash from its input
+        # optional callable hook(kind, thunk) that runs every library call of a
+        # pass; kind is "layer" (the rank's own layer calls), "sum" (the
+        # all-reduce stand-in) or "loss" (the vocabulary-parallel loss calls).
+        # Timing code uses it to bracket the calls; it must call thunk() once.
+        self.hook = None
         self.device = torch.device(device)
         dt = cfg.dtype
         self.tdtype = torch.bfloat16 if dt == "bf16" else torch.float32
@@ -149,8 +154,13 @@ class LayerStep:
         self.exchanges = 0
         self.dloss = 1.0
 
+    def _call(self, kind, fn, *args, **kw):
+        if self.hook is None:
+            return fn(*args, **kw)
+        return self.hook(kind, lambda: fn(*args, **kw))
+
     def _gather(self, src, n_src, row_bytes, dst, stream=None):
-        B.tpl_rows_gather(src, n_src, self.shared["loss_rows_idx"], self.NL, row_bytes, dst, stream)
+        self._call("loss", B.tpl_rows_gather, src, n_src, self.shared["loss_rows_idx"], self.NL, row_bytes, dst, stream)
         return dst
 
     # -------------------------------------------------------------- exchanges
@@ -158,18 +168,18 @@ class LayerStep:
         """All-reduce stand-in: out = residual + bias + sum of every rank's `key`
         tensor (this GPU's ranks, then the stand-in peers)."""
         parts = [st.tensors[key] for st in self.states] + self.peers
-        B.shard_partial_sum(self.states[0].desc, parts, bias, residual, out, self.N, self.cfg.hidden, stream)
+        self._call("sum", B.shard_partial_sum, self.states[0].desc, parts, bias, residual, out, self.N, self.cfg.hidden, stream)
         self.exchanges += 1
 
     # -------------------------------------------------------------- passes
     def forward(self, stream=None):
         sh = self.shared
         for st in self.states:
-            B.tp_layer_shard_fwd(st.desc, B.TPL_BLOCK_ATTN, sh["x"], st.attn, st.tensors["part_attn"],
+            self._call("layer", B.tp_layer_shard_fwd, st.desc, B.TPL_BLOCK_ATTN, sh["x"], st.attn, st.tensors["part_attn"],
                                  st.tensors["saved_attn"], stream)
         self._sum("part_attn", sh["b_o"], sh["x"], sh["h1"], stream)
         for st in self.states:
-            B.tp_layer_shard_fwd(st.desc, B.TPL_BLOCK_MLP, sh["h1"], st.mlp, st.tensors["part_mlp"],
+            self._call("layer", B.tp_layer_shard_fwd, st.desc, B.TPL_BLOCK_MLP, sh["h1"], st.mlp, st.tensors["part_mlp"],
                                  st.tensors["saved_mlp"], stream)
         self._sum("part_mlp", sh["b_2"], sh["h1"], sh["out"], stream)
 
@@ -189,11 +199,11 @@ class LayerStep:
             self._gather(sh["targets"], self.N, 4, sh["targets_l"], stream)
         hidden, targets = self._loss_inputs()
         for st in self.states:
-            B.vocab_parallel_xent_fwd(st.tensors["xdesc"], B.TPL_XENT_LOCAL, hidden=hidden, emb=st.tensors["emb"],
+            self._call("loss", B.vocab_parallel_xent_fwd, st.tensors["xdesc"], B.TPL_XENT_LOCAL, hidden=hidden, emb=st.tensors["emb"],
                                       targets=targets, loss_mask=None, logits=st.tensors["logits"],
                                       stats=st.tensors["stats"], stream=stream)
         all_stats = self._stats_in_rank_order()
-        B.vocab_parallel_xent_fwd(self.states[0].tensors["xdesc"], B.TPL_XENT_FINISH, targets=targets,
+        self._call("loss", B.vocab_parallel_xent_fwd, self.states[0].tensors["xdesc"], B.TPL_XENT_FINISH, targets=targets,
                                   loss_mask=None, all_stats=all_stats, lse=sh["lse"], loss_rows=sh["loss_rows"],
                                   loss=sh["loss"], stream=stream)
 
@@ -208,11 +218,11 @@ class LayerStep:
         for st in self.states:
             t = st.tensors
             dh = t["dH"] if self.loss_idx is None else t["dH_l"]
-            B.vocab_parallel_xent_bwd(t["xdesc"], hidden, t["emb"], targets, None, t["logits"], sh["lse"],
+            self._call("loss", B.vocab_parallel_xent_bwd, t["xdesc"], hidden, t["emb"], targets, None, t["logits"], sh["lse"],
                                       sh["loss"], self.dloss, dh, t["d_emb"], stream)
             if self.loss_idx is not None:   # dH of the loss rows back to every row, zeros elsewhere
                 es = 2 if self.cfg.dtype == "bf16" else 4
-                B.tpl_rows_expand(dh, self.NL, sh["loss_rows_pos"], self.N, self.cfg.hidden * es, t["dH"], stream)
+                self._call("loss", B.tpl_rows_expand, dh, self.NL, sh["loss_rows_pos"], self.N, self.cfg.hidden * es, t["dH"], stream)
         self._sum("dH", None, sh["R"], sh["dout"], stream)
 
     def poison_saved(self):
@@ -227,21 +237,21 @@ class LayerStep:
         shard = B.TPL_BWD_SHARD_RECOMPUTE if self.recompute else B.TPL_BWD_SHARD
         for st in self.states:
             t = st.tensors
-            B.tp_layer_shard_bwd(st.desc, B.TPL_BLOCK_MLP, shard, sh["dout"], None, sh["h1"], st.mlp,
+            self._call("layer", B.tp_layer_shard_bwd, st.desc, B.TPL_BLOCK_MLP, shard, sh["dout"], None, sh["h1"], st.mlp,
                                  t["saved_mlp"], t["dln_mlp"], None,
                                  B.block_grads(t["d_w_1"], t["d_b_1"], t["d_w_2"]), stream)
         self._sum("dln_mlp", None, None, sh["dz_sum"], stream)
         st0 = self.states[0]   # the replicated part is identical on every rank: run it once
-        B.tp_layer_shard_bwd(st0.desc, B.TPL_BLOCK_MLP, B.TPL_BWD_REPLICATED, sh["dout"], sh["dz_sum"], sh["h1"],
+        self._call("layer", B.tp_layer_shard_bwd, st0.desc, B.TPL_BLOCK_MLP, B.TPL_BWD_REPLICATED, sh["dout"], sh["dz_sum"], sh["h1"],
                              st0.mlp, st0.tensors["saved_mlp"], None, sh["dh1"],
                              B.block_grads(d_ln_g=sh["d_ln2_g"], d_ln_b=sh["d_ln2_b"], d_b_out=sh["d_b_2"]), stream)
         for st in self.states:
             t = st.tensors
-            B.tp_layer_shard_bwd(st.desc, B.TPL_BLOCK_ATTN, shard, sh["dh1"], None, sh["x"], st.attn,
+            self._call("layer", B.tp_layer_shard_bwd, st.desc, B.TPL_BLOCK_ATTN, shard, sh["dh1"], None, sh["x"], st.attn,
                                  t["saved_attn"], t["dln_attn"], None,
                                  B.block_grads(t["d_w_qkv"], t["d_b_qkv"], t["d_w_o"]), stream)
         self._sum("dln_attn", None, None, sh["dy_sum"], stream)
-        B.tp_layer_shard_bwd(st0.desc, B.TPL_BLOCK_ATTN, B.TPL_BWD_REPLICATED, sh["dh1"], sh["dy_sum"], sh["x"],
+        self._call("layer", B.tp_layer_shard_bwd, st0.desc, B.TPL_BLOCK_ATTN, B.TPL_BWD_REPLICATED, sh["dh1"], sh["dy_sum"], sh["x"],
                              st0.attn, st0.tensors["saved_attn"], None, sh["dx"],
                              B.block_grads(d_ln_g=sh["d_ln1_g"], d_ln_b=sh["d_ln1_b"], d_b_out=sh["d_b_o"]), stream)
 

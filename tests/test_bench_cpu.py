@@ -62,6 +62,7 @@ def test_kernel_family(kernel, family):
 
 
 def test_trace_command_names_the_workload():
-    assert "--config" not in bench.trace_cmd(bench.DEFAULT_WORKLOAD)
+    assert bench.DEFAULT_WORKLOAD == "gpt_175b_t8"
+    assert "bench.py --config gpt2_355m_t1 --steps 5" in bench.trace_cmd("gpt2_355m_t1")
     cmd = bench.trace_cmd("gpt_175b_t8")
     assert "bench.py --config gpt_175b_t8 --steps 5" in cmd and cmd.startswith("cd /tmp && rocprofv3 --kernel-trace")
