@@ -249,6 +249,24 @@ tpl_status vocab_parallel_embedding_fwd(const tpl_desc* desc, const int32_t* tok
 tpl_status vocab_parallel_embedding_bwd(const tpl_desc* desc, const int32_t* tokens, const void* d_out,
                                         float* d_emb_in, void* workspace, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * backward as vocab_parallel_embedding_bwd, with its workspace taken from a
+ * device array of TPL_NOALLOC_SCRATCH_BYTES inside the library (one per GPU,
+ * held until the process ends) instead of a workspace argument. It calls no
+ * allocating routine. Limit: vocab_parallel_embedding_ws_bytes(desc) <=
+ * TPL_NOALLOC_SCRATCH_BYTES (16 B per row plus 4 B per vocabulary row of the
+ * rank, rounded up to 256 B), else TPL_ERR_UNSUPPORTED before any launch.
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap on one
+ * GPU (different streams, or several threads) race and must be serialised
+ * by the caller. The first call on a device looks the array's address up
+ * (TPL_ERR_HIP if that fails). Results are bitwise those of
+ * vocab_parallel_embedding_bwd. */
+#define TPL_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+tpl_status vocab_parallel_embedding_bwd_noalloc(const tpl_desc* desc, const int32_t* tokens, const void* d_out,
+                                                float* d_emb_in, void* stream);
+
 /* Vocabulary-parallel cross-entropy backward for this rank (guide page
  * "From Transformer splitting to communication optimisation", section 3.3:
  * the output layer split along the vocabulary with the gather deferred into

@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L.vocab_parallel_embedding_ws_bytes.argtypes = [P(TplDesc)]
         L.vocab_parallel_embedding_fwd.argtypes = [P(TplDesc), _VP, _VP, _VP, _VP]
         L.vocab_parallel_embedding_bwd.argtypes = [P(TplDesc), _VP, _VP, _VP, _VP, _VP]
+        L.vocab_parallel_embedding_bwd_noalloc.argtypes = [P(TplDesc), _VP, _VP, _VP, _VP]
         L.tp_layer_shard_fwd.argtypes = [P(TplDesc), ctypes.c_int, _VP, P(TplBlockParams), _VP, _VP, _VP]
         L.shard_partial_sum.argtypes = [P(TplDesc), P(ctypes.c_void_p), _I32, _VP, _VP, _VP, _I64, _I32, _VP]
         L.tp_layer_shard_bwd.argtypes = [P(TplDesc), ctypes.c_int, ctypes.c_int, _VP, _VP, _VP,
@@ -99,7 +100,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("tp_layer_saved_bytes", "tp_layer_shard_fwd", "shard_partial_sum", "tp_layer_shard_bwd",
             "vocab_parallel_xent_stats_bytes", "vocab_parallel_xent_fwd",
-            "vocab_parallel_embedding_ws_bytes", "vocab_parallel_embedding_fwd", "vocab_parallel_embedding_bwd", "vocab_parallel_xent_bwd", "tpl_rows_gather", "tpl_rows_expand", "tpl_gemm", "tpl_trace_enable",
+            "vocab_parallel_embedding_ws_bytes", "vocab_parallel_embedding_fwd", "vocab_parallel_embedding_bwd",
+            "vocab_parallel_embedding_bwd_noalloc", "vocab_parallel_xent_bwd", "tpl_rows_gather", "tpl_rows_expand", "tpl_gemm", "tpl_trace_enable",
             "tpl_trace_read", "tpl_trace_kernel_name", "tpl_status_string")
 
 
@@ -164,6 +166,14 @@ def vocab_parallel_embedding_fwd(desc, tokens, emb_in, x_partial, stream=None):
 def vocab_parallel_embedding_bwd(desc, tokens, d_out, d_emb_in, workspace, stream=None):
     _check("vocab_parallel_embedding_bwd", lib().vocab_parallel_embedding_bwd(
         ctypes.byref(desc), _ptr(tokens), _ptr(d_out), _ptr(d_emb_in), _ptr(workspace), _stream(stream)))
+
+
+def vocab_parallel_embedding_bwd_noalloc(desc, tokens, d_out, d_emb_in, stream=None):
+    _check("vocab_parallel_embedding_bwd_noalloc", lib().vocab_parallel_embedding_bwd_noalloc(
+        ctypes.byref(desc), _ptr(tokens), _ptr(d_out), _ptr(d_emb_in), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20   # TPL_NOALLOC_SCRATCH_BYTES of include/tp_layer.h
 
 
 def tp_layer_shard_fwd(desc, block, x, params: TplBlockParams, partial, saved, stream=None):

@@ -492,6 +492,20 @@ tpl_status vocab_parallel_embedding_bwd(const tpl_desc* desc, const int32_t* tok
                                        (int)m.vr, workspace, static_cast<hipStream_t>(stream)));
 }
 
+tpl_status vocab_parallel_embedding_bwd_noalloc(const tpl_desc* desc, const int32_t* tokens, const void* d_out,
+                                                float* d_emb_in, void* stream) {
+  static_assert(TPL_NOALLOC_SCRATCH_BYTES == kNoAllocScratchBytes, "header and library disagree on the limit");
+  Dims m;
+  tpl_status st = check_desc(desc, &m);
+  if (st != TPL_OK) return st;
+  if (!ok_ptr(tokens) || !ok_ptr(d_out) || !ok_ptr(d_emb_in)) return TPL_ERR_INVALID_ARG;
+  if (round256(embedding_ws_bytes(m.N, (int)m.vr)) > kNoAllocScratchBytes) return TPL_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return TPL_ERR_HIP;
+  return from_hip(launch_embedding_bwd(m.dt, tokens, d_out, d_emb_in, m.N, (int)m.h, (int64_t)desc->rank * m.vr,
+                                       (int)m.vr, ws, static_cast<hipStream_t>(stream)));
+}
+
 static bool ok_ptr4(const void* p) { return p != nullptr && reinterpret_cast<uintptr_t>(p) % 4 == 0; }
 
 tpl_status tpl_rows_gather(const void* src, int64_t n_src, const int32_t* rows, int64_t n, int64_t row_bytes, void* dst,

@@ -10,6 +10,7 @@
 // reads N*h elements once and writes the V_r*h fp32 table once (every row,
 // zero where no id points).
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -283,6 +284,41 @@ int index_bits(int n) {
 }  // namespace
 
 size_t embedding_ws_bytes(int64_t rows, int vr) { return ((size_t)rows * 4 + (size_t)vr + 64) * 4; }
+
+// ------------------------------------------------------------------ allocation-free backward
+// The workspace of the allocation-free backward lives in this file-scope
+// device array, one copy per GPU, held until the process ends. Host code
+// never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current and
+// kept per device. Nothing in it must start at zero: the sort writes every
+// key and value it reads back, and the gradient kernel accepts a segment
+// start only where it points at the first occurrence of its key (the
+// multi-pass sort clears the segment table itself).
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_embedding_fwd(int dtype, const int32_t* tokens, const void* emb, void* out, int64_t rows, int cols,
                                 int64_t v0, int vr, hipStream_t s) {

@@ -126,6 +126,11 @@ hipError_t launch_xent_dlogits(int dtype, void* logits, int64_t rows, int vr,
 // ------------------------------------------------------------------ input embedding
 // Workspace bytes of the backward (sort keys / values twice, segment starts).
 size_t embedding_ws_bytes(int64_t rows, int vr);
+// The allocation-free backward's workspace: a device array of
+// kNoAllocScratchBytes per GPU; *ptr = its address on the current device
+// (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+hipError_t noalloc_scratch(void** ptr);
 // Row gather / expand of a masked loss's rows (row_bytes a multiple of 4):
 // gather: dst[i] = src[rows[i]] (i < n; an index outside [0, n_src) gives zeros);
 // expand: dst[r] = src[pos[r]] if 0 <= pos[r] < n_src, else zeros (r < n_dst).

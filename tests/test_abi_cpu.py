@@ -116,3 +116,15 @@ def test_row_gather_and_expand_reject_bad_arguments(args):
     L = B.lib()
     assert L.tpl_rows_gather(*args, None) == B.TPL_ERR_INVALID_ARG
     assert L.tpl_rows_expand(*args, None) == B.TPL_ERR_INVALID_ARG
+
+
+def test_noalloc_embedding_backward_refuses_oversized_workspace_on_the_host():
+    """The allocation-free embedding backward refuses, before any launch, a
+    workload whose workspace exceeds the library's array (1.1M vocabulary
+    rows of the rank need 4.4 MB, over TPL_NOALLOC_SCRATCH_BYTES = 4 MiB)."""
+    d = good_desc(vocab=2_200_000)
+    assert B.vocab_parallel_embedding_ws_bytes(d) > B.NOALLOC_SCRATCH_BYTES
+    rc = B.lib().vocab_parallel_embedding_bwd_noalloc(ctypes.byref(d), 16, 16, 16, None)
+    assert rc == B.TPL_ERR_UNSUPPORTED
+    rc = B.lib().vocab_parallel_embedding_bwd_noalloc(ctypes.byref(good_desc()), None, 16, 16, None)
+    assert rc == B.TPL_ERR_INVALID_ARG
