@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (AMD data sheet)
 PEAK_HBM_GBS = 8000.0                           # MI355X HBM3E
-MFMA_KERNELS = {"gemm_nt", "gemm_nn", "gemm_tn", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"}
+MFMA_KERNELS = {"gemm_nt", "gemm_nn", "gemm_tn", "gemm_pair", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"}
 METRIC = "TFLOP/s per TP layer-shard fwd+bwd (bf16) and % of MI355X MFMA peak"
 
 
@@ -261,6 +261,8 @@ PROFILE_CMDS = {
 def kernel_family(name: str) -> str:
     """Map a rocprofv3 kernel name (mangled or demangled) to the trace names."""
     import re
+    if "gemm_pair" in name:           # an activation- and a weight-gradient product in one launch
+        return "gemm_pair"
     if "gemm" in name:
         m = re.search(r"gemm_\w*kernel<([^>]*)>", name)
         if m:

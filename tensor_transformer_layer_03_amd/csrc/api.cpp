@@ -107,6 +107,8 @@ Saved saved_layout(const Dims& m, tpl_block block) {
     sz[S_DU] = m.N * m.fr * es;
     ws = std::max(ws, colsum_ws_floats(m.N, m.fr));
     ws = std::max(ws, (size_t)gemm_colpart_chunks(m.dt, m.N, m.fr) * m.fr);   // db_1 partials of the du product
+    if (m.dt == DT_BF16)                                                      // ... when paired with dW_2
+      ws = std::max(ws, (size_t)gemm_pair_colpart_chunks(m.N) * m.fr);
     ws = std::max(ws, gemm_ws_floats(m.dt, m.h, m.fr, m.N));       // dW_2
     ws = std::max(ws, gemm_ws_floats(m.dt, m.fr, m.h, m.N));       // dW_1
   }
@@ -156,7 +158,7 @@ const char* const kKernelNames[K_COUNT] = {
     "gemm_nt", "gemm_nn", "gemm_tn", "attn_fwd", "attn_bwd_pre", "attn_bwd_dq", "attn_bwd_dkdv",
     "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_cols", "colsum", "colsum_final", "partial_sum",
     "xent_stats", "xent_finish", "xent_dlogits", "xent_merge", "embedding_fwd", "embedding_sort", "embedding_bwd",
-    "rows_gather", "rows_expand"};
+    "rows_gather", "rows_expand", "gemm_pair"};
 
 }  // namespace
 
@@ -366,13 +368,20 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     a.lse = slot<float>(saved, L, S_LSE);
     a.dctx = dctx; a.dqkv = dqkv; a.delta = slot<float>(saved, L, S_DELTA);
     TPL_TRY(launch_attn_bwd(a, s));
-    // dW_qkv = dqkv^T y ; db_qkv = colsum(dqkv) ; d_ln = dqkv W_qkv
+    // dW_qkv = dqkv^T y ; db_qkv = colsum(dqkv) ; d_ln = dqkv W_qkv (the two products
+    // in one launch when that fills the CUs better)
     GemmDesc gq = gemm(m, false, false, 3 * m.hr, m.h, m.N, dqkv, 3 * m.hr, y, m.h, gr->d_w_in, m.h);
     gq.c_f32 = true;
     gq.ws = ws;
-    TPL_TRY(launch_gemm(gq, s));
-    TPL_TRY(launch_colsum(m.dt, dqkv, 3 * m.hr, m.N, 3 * m.hr, gr->d_b_in, ws, s));
-    TPL_TRY(launch_gemm(gemm(m, true, false, m.N, m.h, 3 * m.hr, dqkv, 3 * m.hr, p->w_in, m.h, d_ln_partial, m.h), s));
+    const GemmDesc gqd = gemm(m, true, false, m.N, m.h, 3 * m.hr, dqkv, 3 * m.hr, p->w_in, m.h, d_ln_partial, m.h);
+    if (gemm_pair_wanted(gqd, gq)) {
+      TPL_TRY(launch_gemm_pair(gqd, gq, s));
+      TPL_TRY(launch_colsum(m.dt, dqkv, 3 * m.hr, m.N, 3 * m.hr, gr->d_b_in, ws, s));
+    } else {
+      TPL_TRY(launch_gemm(gq, s));
+      TPL_TRY(launch_colsum(m.dt, dqkv, 3 * m.hr, m.N, 3 * m.hr, gr->d_b_in, ws, s));
+      TPL_TRY(launch_gemm(gqd, s));
+    }
   } else {
     void* gp = slot<char>(saved, L, S_GP);
     void* act = slot<char>(saved, L, S_ACT);
@@ -383,20 +392,34 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     g.epi = EPI_DGELU;
     g.C2 = gp;
     g.ldc2 = m.fr;
-    const int64_t cp = gemm_colpart_chunks(m.dt, m.N, m.fr);
-    if (cp > 0) g.colpart = ws;
-    TPL_TRY(launch_gemm(g, s));
-    if (cp > 0) TPL_TRY(launch_colsum_final(ws, cp, m.fr, gr->d_b_in, s));
     GemmDesc g2 = gemm(m, false, false, m.h, m.fr, m.N, dy, m.h, act, m.fr, gr->d_w_out, m.fr);
     g2.c_f32 = true;
     g2.ws = ws;
-    TPL_TRY(launch_gemm(g2, s));
+    // the fc2 activation and weight gradients in one launch when that fills the
+    // CUs better (the column partials then come in the paired tile's row blocks)
+    const bool pair2 = gemm_pair_wanted(g, g2);
+    const int64_t cp = pair2 ? gemm_pair_colpart_chunks(m.N) : gemm_colpart_chunks(m.dt, m.N, m.fr);
+    if (cp > 0) g.colpart = ws;
+    if (pair2) {
+      TPL_TRY(launch_gemm_pair(g, g2, s));
+      if (cp > 0) TPL_TRY(launch_colsum_final(ws, cp, m.fr, gr->d_b_in, s));
+    } else {
+      TPL_TRY(launch_gemm(g, s));
+      if (cp > 0) TPL_TRY(launch_colsum_final(ws, cp, m.fr, gr->d_b_in, s));
+      TPL_TRY(launch_gemm(g2, s));
+    }
     GemmDesc g1 = gemm(m, false, false, m.fr, m.h, m.N, du, m.fr, y, m.h, gr->d_w_in, m.h);
     g1.c_f32 = true;
     g1.ws = ws;
-    TPL_TRY(launch_gemm(g1, s));
-    if (cp == 0) TPL_TRY(launch_colsum(m.dt, du, m.fr, m.N, m.fr, gr->d_b_in, ws, s));
-    TPL_TRY(launch_gemm(gemm(m, true, false, m.N, m.h, m.fr, du, m.fr, p->w_in, m.h, d_ln_partial, m.h), s));
+    const GemmDesc g1d = gemm(m, true, false, m.N, m.h, m.fr, du, m.fr, p->w_in, m.h, d_ln_partial, m.h);
+    if (gemm_pair_wanted(g1d, g1)) {
+      TPL_TRY(launch_gemm_pair(g1d, g1, s));
+      if (cp == 0) TPL_TRY(launch_colsum(m.dt, du, m.fr, m.N, m.fr, gr->d_b_in, ws, s));
+    } else {
+      TPL_TRY(launch_gemm(g1, s));
+      if (cp == 0) TPL_TRY(launch_colsum(m.dt, du, m.fr, m.N, m.fr, gr->d_b_in, ws, s));
+      TPL_TRY(launch_gemm(g1d, s));
+    }
   }
   return TPL_OK;
 }

@@ -31,6 +31,8 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
+#include <vector>
 
 #include "common.h"
 #include "kernels.h"
@@ -588,20 +590,24 @@ struct CStage {
   }
 };
 
+// LDS of one workgroup of the two-stage kernel: two stages of an A and a B tile.
+template <int BM, int BN, bool DMA>
+constexpr int body_smem_bytes() { return 2 * (tile_bytes<BM, DMA>() + tile_bytes<BN, DMA>()); }
+
+// One output tile (workgroup number bid of the product's grid); smem holds
+// body_smem_bytes<BM, BN, DMA>() bytes.
 template <int BM, int BN, int WGM, int WGN, bool A_K, bool B_K, bool DMA, int EPI, typename TC>
-__device__ __forceinline__ void gemm_bf16_body(Args g) {
+__device__ __forceinline__ void gemm_bf16_body(Args g, int bid, char* smem) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN, TM = WTM / 32, TN = WTN / 32;
   constexpr int kBOff = tile_bytes<BM, DMA>();                 // B tile offset in a stage
   constexpr int kStage = kBOff + tile_bytes<BN, DMA>();
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave % WGM, wn = wave / WGM;
 
   const int nblk = g.tiles_m * g.tiles_n;
-  int bid = blockIdx.x;
   if (g.splits > 1) {
     // split-K: workgroup (split, tile) takes K range [split*kchunk, ...);
     // split 0 writes C, split s the workspace slice s-1 (summed afterwards
@@ -814,7 +820,29 @@ __device__ __forceinline__ void gemm_bf16_body(Args g) {
 
 template <int BM, int BN, int WGM, int WGN, bool A_K, bool B_K, bool DMA, int EPI, typename TC>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
-  gemm_bf16_body<BM, BN, WGM, WGN, A_K, B_K, DMA, EPI, TC>(g);
+  __shared__ __attribute__((aligned(1024))) char smem[body_smem_bytes<BM, BN, DMA>()];
+  gemm_bf16_body<BM, BN, WGM, WGN, A_K, B_K, DMA, EPI, TC>(g, blockIdx.x, smem);
+}
+
+// Two independent products of a block's backward in one launch, both on the
+// 256x256 eight-wave tile with register-staged operands: workgroups [0, n0)
+// take product 0's tiles (the longer ones in K, so they start first),
+// [n0pad, n0pad + tiles of product 1) product 1's. n0pad is n0 rounded up to
+// a multiple of 8 (the padding workgroups exit at once) so that both products
+// keep their XCD-aware tile walk. One grid lets the short tiles of one product
+// fill the compute units the other leaves idle in its last round.
+template <int WGM0, int WGN0, bool AK0, bool BK0, int EPI0, typename TC0, int WGM1, int WGN1, bool AK1, bool BK1,
+          int EPI1, typename TC1>
+__global__ __launch_bounds__(512) void gemm_pair_kernel(Args g0, Args g1, int n0, int n0pad) {
+  static_assert(WGM0 * WGN0 == 8 && WGM1 * WGN1 == 8, "both products take 8 waves");
+  __shared__ __attribute__((aligned(1024))) char smem[body_smem_bytes<256, 256, false>()];
+  const int bid = blockIdx.x;
+  if (bid < n0pad) {
+    if (bid >= n0) return;
+    gemm_bf16_body<256, 256, WGM0, WGN0, AK0, BK0, false, EPI0, TC0>(g0, bid, smem);
+  } else {
+    gemm_bf16_body<256, 256, WGM1, WGN1, AK1, BK1, false, EPI1, TC1>(g1, bid - n0pad, smem);
+  }
 }
 
 // The same product as the first pass of a tail split (the last tile rows
@@ -822,7 +850,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_kernel(Args g) {
 // trace tells the two passes apart.
 template <int BM, int BN, int WGM, int WGN, bool A_K, bool B_K, bool DMA, int EPI, typename TC>
 __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bf16_tail_kernel(Args g) {
-  gemm_bf16_body<BM, BN, WGM, WGN, A_K, B_K, DMA, EPI, TC>(g);
+  __shared__ __attribute__((aligned(1024))) char smem[body_smem_bytes<BM, BN, DMA>()];
+  gemm_bf16_body<BM, BN, WGM, WGN, A_K, B_K, DMA, EPI, TC>(g, blockIdx.x, smem);
 }
 
 // ------------------------------------------- multi-stage K pipeline (K-major operands)
@@ -1521,6 +1550,42 @@ hipError_t run_tn_tail(const GemmDesc& d, const TailSplit& t, hipStream_t s) {
   return run_v2<256, 256, 2, 4, false, false, EPI_NONE, float>(w, s);
 }
 
+// Arguments of one product of a paired launch (256x256 tiles, no split).
+Args pair_args(const GemmDesc& d) {
+  Args a{};
+  a.A = static_cast<const char*>(d.A); a.lda = d.lda;
+  a.B = static_cast<const char*>(d.B); a.ldb = d.ldb;
+  a.C = static_cast<char*>(d.C); a.ldc = d.ldc;
+  a.C2 = static_cast<char*>(d.C2); a.ldc2 = d.ldc2;
+  a.bias = static_cast<const char*>(d.bias);
+  a.M = (int)d.M; a.N = (int)d.N; a.K = (int)d.K;
+  a.tiles_m = (a.M + 255) / 256;
+  a.tiles_n = (a.N + 255) / 256;
+  a.splits = 1;
+  a.kchunk = a.K;
+  a.ws = nullptr;
+  a.colpart = d.epi == EPI_DGELU ? d.colpart : nullptr;
+  return a;
+}
+
+// Makespan (in units of one 256x256 tile step of depth 1) of list scheduling
+// tiles on `cus` compute units in grid order: groups of (count, depth K).
+double list_makespan(const int64_t (*groups)[2], int ngroups, int cus) {
+  std::vector<double> free_at((size_t)cus, 0.0);
+  std::make_heap(free_at.begin(), free_at.end(), std::greater<double>());
+  double end = 0.0;
+  for (int g = 0; g < ngroups; ++g) {
+    for (int64_t i = 0; i < groups[g][0]; ++i) {
+      std::pop_heap(free_at.begin(), free_at.end(), std::greater<double>());
+      const double t = free_at.back() + (double)groups[g][1];
+      free_at.back() = t;
+      std::push_heap(free_at.begin(), free_at.end(), std::greater<double>());
+      end = std::max(end, t);
+    }
+  }
+  return end;
+}
+
 template <typename T>
 hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
   if (d.a_kmajor && d.b_kmajor) {
@@ -1597,6 +1662,68 @@ int64_t gemm_colpart_chunks(int dtype, int64_t M, int64_t N) {
   const int rc = t.bm / (nt / t.bn);                                  // rows per partial block
   return (M + rc - 1) / rc;
 }
+// Pair a block's activation-gradient product dg (A K-major, B MN-major, bf16
+// out, EPI_NONE or EPI_DGELU) with its weight-gradient product wg (both
+// MN-major, fp32 out) in one launch when neither is split over K on its own
+// and list scheduling of both tile sets on the CUs (longer tiles first)
+// finishes at least 5% sooner than dg's own rounds plus wg perfectly packed
+// (what its tail split approaches). 175B rank: the MLP and QKV pairs, whose
+// activation gradients leave half or a quarter of the CUs idle in their last
+// round. TPL_GEMM_PAIR=0/1 forces the choice (tests).
+bool gemm_pair_wanted(const GemmDesc& dg, const GemmDesc& wg) {
+  if (dg.dtype != DT_BF16 || wg.dtype != DT_BF16) return false;
+  if (!dg.a_kmajor || dg.b_kmajor || dg.c_f32 || (dg.epi != EPI_NONE && dg.epi != EPI_DGELU)) return false;
+  if (wg.a_kmajor || wg.b_kmajor || !wg.c_f32 || wg.epi != EPI_NONE || wg.ldc != wg.N) return false;
+  if (dg.M <= 0 || dg.N <= 0 || dg.K <= 0 || wg.M <= 0 || wg.N <= 0 || wg.K <= 0) return false;
+  if (const char* f = getenv("TPL_GEMM_PAIR")) return f[0] == '1';
+  if (getenv("TPL_GEMM_TILE")) return false;
+  if (dg.epi == EPI_NONE && splitk_dgrad_for(dg.dtype, dg.M, dg.N, dg.K, ~size_t(0)).splits > 1) return false;
+  if (splitk_for(wg.dtype, wg.M, wg.N, wg.K).splits > 1) return false;
+  const int cus = device_cus();
+  const int64_t td = ((dg.M + 255) / 256) * ((dg.N + 255) / 256), tw = ((wg.M + 255) / 256) * ((wg.N + 255) / 256);
+  int64_t groups[2][2] = {{td, dg.K}, {tw, wg.K}};
+  if (wg.K > dg.K) {
+    std::swap(groups[0][0], groups[1][0]);
+    std::swap(groups[0][1], groups[1][1]);
+  }
+  const int64_t one[1][2] = {{td, dg.K}};
+  const double paired = list_makespan(groups, 2, cus);
+  const double apart = list_makespan(one, 1, cus) + (double)tw * (double)wg.K / cus;
+  return paired < 0.95 * apart;
+}
+
+// Column-partial blocks the paired activation-gradient product writes for
+// EPI_DGELU (128 rows each: the 256x256 tile's eight waves as 4 x 2).
+int64_t gemm_pair_colpart_chunks(int64_t M) { return (M + 127) / 128; }
+
+hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, hipStream_t s) {
+  TraceScope trace(K_GEMM_PAIR, s, 2.0 * (double)dg.M * dg.N * dg.K + 2.0 * (double)wg.M * wg.N * wg.K);
+  if (dg.dtype != DT_BF16 || wg.dtype != DT_BF16) return hipErrorInvalidValue;
+  const Args a0 = pair_args(dg), a1 = pair_args(wg);
+  const int64_t t0 = (int64_t)a0.tiles_m * a0.tiles_n, t1 = (int64_t)a1.tiles_m * a1.tiles_n;
+  if (t0 + t1 + 8 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const bool wg_first = wg.K > dg.K;   // the longer tiles start first
+  const int n0 = (int)(wg_first ? t1 : t0), n0pad = (n0 + 7) / 8 * 8, n1 = (int)(wg_first ? t0 : t1);
+  if (n0 + n1 == 0) return hipSuccess;
+  const dim3 grid((unsigned)(n0pad + n1)), block(512);
+  if (wg_first) {
+    if (dg.epi == EPI_DGELU)
+      hipLaunchKernelGGL((gemm_pair_kernel<2, 4, false, false, EPI_NONE, float, 4, 2, true, false, EPI_DGELU, bf16>),
+                         grid, block, 0, s, a1, a0, n0, n0pad);
+    else
+      hipLaunchKernelGGL((gemm_pair_kernel<2, 4, false, false, EPI_NONE, float, 4, 2, true, false, EPI_NONE, bf16>),
+                         grid, block, 0, s, a1, a0, n0, n0pad);
+  } else {
+    if (dg.epi == EPI_DGELU)
+      hipLaunchKernelGGL((gemm_pair_kernel<4, 2, true, false, EPI_DGELU, bf16, 2, 4, false, false, EPI_NONE, float>),
+                         grid, block, 0, s, a0, a1, n0, n0pad);
+    else
+      hipLaunchKernelGGL((gemm_pair_kernel<4, 2, true, false, EPI_NONE, bf16, 2, 4, false, false, EPI_NONE, float>),
+                         grid, block, 0, s, a0, a1, n0, n0pad);
+  }
+  return hipGetLastError();
+}
+
 size_t xent_part_floats(int64_t M, int64_t N) { return (size_t)((N + 127) / 128) * (size_t)M * 2; }
 
 int device_cu_count() { return device_cus(); }

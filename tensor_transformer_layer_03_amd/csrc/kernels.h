@@ -14,7 +14,7 @@ enum KernelId {
   K_GEMM_NT = 0, K_GEMM_NN, K_GEMM_TN, K_ATTN_FWD, K_ATTN_BWD_PRE, K_ATTN_BWD_DQ,
   K_ATTN_BWD_DKDV, K_LN_FWD, K_LN_BWD, K_LN_BWD_COLS, K_COLSUM, K_COLSUM_FINAL,
   K_PARTIAL_SUM, K_XENT_STATS, K_XENT_FINISH, K_XENT_DLOGITS, K_XENT_MERGE, K_EMB_FWD, K_EMB_SORT, K_EMB_BWD,
-  K_ROWS_GATHER, K_ROWS_EXPAND,
+  K_ROWS_GATHER, K_ROWS_EXPAND, K_GEMM_PAIR,
   K_COUNT
 };
 const char* kernel_name(int id);
@@ -59,6 +59,14 @@ struct GemmDesc {
   float* colpart;
 };
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
+// A block's activation-gradient product dg (A K-major, B MN-major, storage
+// type out, EPI_NONE or EPI_DGELU) and its weight-gradient product wg (both
+// MN-major, fp32 out, ldc == N) in one launch on 256x256 tiles, no split
+// over K; gemm_pair_wanted says when that beats two launches, and an
+// EPI_DGELU dg then writes gemm_pair_colpart_chunks(dg.M) column partials.
+bool gemm_pair_wanted(const GemmDesc& dg, const GemmDesc& wg);
+int64_t gemm_pair_colpart_chunks(int64_t M);
+hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, hipStream_t s);
 // Floats of split-K workspace the product (M, N, K) with both operands MN-major
 // and an fp32 output takes (0: it is not split).
 size_t gemm_ws_floats(int dtype, int64_t M, int64_t N, int64_t K);

@@ -117,6 +117,18 @@ def test_attention_wave_forms(cfg, split, monkeypatch):
     _assert_ok(report)
 
 
+@pytest.mark.parametrize("pair", ["0", "1"])
+@pytest.mark.parametrize("cfg", [SMALL[1], SMALL[2], SMALL[3]], ids=lambda c: c.name)
+def test_paired_backward_products(cfg, pair, monkeypatch):
+    """Each block's activation- and weight-gradient products in one launch
+    (chosen automatically where it fills the CUs better, e.g. the 175B rank;
+    forced on and off here on ragged shapes, with the fc2 pair's GeLU'
+    epilogue and bias-gradient column partials)."""
+    monkeypatch.setenv("TPL_GEMM_PAIR", pair)
+    report, st = check_case(cfg)
+    _assert_ok(report)
+
+
 WIDE = [
     synth.tiny_config("f32", hidden=768, heads=12, head_dim=64, ffn=1536, tp=2, seq=40, micro_batch=2,
                       vocab=128, causal=True, sigma_w=0.05, index=56, name="small_f32_wide_rows"),
