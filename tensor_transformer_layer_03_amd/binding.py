@@ -14,7 +14,9 @@ from typing import Sequence
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtplayer.so")
+# TPL_LIBRARY selects another build of the same library (the AddressSanitizer
+# build of the host code, libtplayer_asan.so, for the CPU tests of the C ABI)
+LIB_PATH = os.environ.get("TPL_LIBRARY") or os.path.join(HERE, "libtplayer.so")
 
 TPL_OK, TPL_ERR_INVALID_ARG, TPL_ERR_UNSUPPORTED, TPL_ERR_HIP = 0, 1, 2, 3
 TPL_F32, TPL_BF16 = 0, 1
