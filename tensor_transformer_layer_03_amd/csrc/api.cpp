@@ -68,6 +68,37 @@ tpl_status from_hip(hipError_t e) { return e == hipSuccess ? TPL_OK : TPL_ERR_HI
     if (e_ != hipSuccess) return TPL_ERR_HIP;                \
   } while (0)
 
+GemmDesc gemm(const Dims& m, bool ak, bool bk, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+              const void* B, int64_t ldb, void* C, int64_t ldc) {
+  GemmDesc g{};
+  g.dtype = m.dt;
+  g.a_kmajor = ak;
+  g.b_kmajor = bk;
+  g.epi = EPI_NONE;
+  g.c_f32 = false;
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda;
+  g.B = B; g.ldb = ldb;
+  g.C = C; g.ldc = ldc;
+  g.C2 = nullptr; g.ldc2 = 0;
+  g.bias = nullptr;
+  return g;
+}
+
+// Workspace floats of a block's paired activation- and weight-gradient
+// products (dg: [dM x dN] over dK; wg: [wM x wN] fp32 over wK), whether or
+// not the pair is taken (the plan's split is fixed either way).
+size_t pair_ws_floats(const Dims& m, int64_t dM, int64_t dN, int64_t dK, int epi, int64_t wM, int64_t wN, int64_t wK) {
+  if (m.dt != DT_BF16) return 0;
+  GemmDesc dg = gemm(m, true, false, dM, dN, dK, nullptr, dK, nullptr, dN, nullptr, dN);
+  dg.epi = epi;
+  GemmDesc wg = gemm(m, false, false, wM, wN, wK, nullptr, wM, nullptr, wN, nullptr, wN);
+  wg.c_f32 = true;
+  PairPlan plan;
+  (void)gemm_pair_plan(dg, wg, &plan);
+  return gemm_pair_ws_floats(dg, wg, plan);
+}
+
 // ------------------------------------------------------------------ saved layout
 // Regions are 256-byte aligned. ATTN: mu, rstd [N] f32; y [N][h]; qkv [N][3hr];
 // ctx [N][hr]; lse [b][a_r][s] f32; then backward scratch: dctx [N][hr],
@@ -101,14 +132,15 @@ Saved saved_layout(const Dims& m, tpl_block block) {
     ws = std::max(ws, gemm_ws_floats(m.dt, m.h, m.hr, m.N));       // dW_o
     ws = std::max(ws, gemm_ws_floats(m.dt, 3 * m.hr, m.h, m.N));   // dW_qkv
     ws = std::max(ws, gemm_dgrad_ws_floats(m.dt, m.N, m.hr, m.h));  // dctx split over K
+    ws = std::max(ws, pair_ws_floats(m, m.N, m.h, 3 * m.hr, EPI_NONE, 3 * m.hr, m.h, m.N));   // d_ln + dW_qkv
   } else {
     sz[S_GP] = m.N * m.fr * es;
     sz[S_ACT] = m.N * m.fr * es;
     sz[S_DU] = m.N * m.fr * es;
     ws = std::max(ws, colsum_ws_floats(m.N, m.fr));
     ws = std::max(ws, (size_t)gemm_colpart_chunks(m.dt, m.N, m.fr) * m.fr);   // db_1 partials of the du product
-    if (m.dt == DT_BF16)                                                      // ... when paired with dW_2
-      ws = std::max(ws, (size_t)gemm_pair_colpart_chunks(m.N) * m.fr);
+    ws = std::max(ws, pair_ws_floats(m, m.N, m.fr, m.h, EPI_DGELU, m.h, m.fr, m.N));   // du + dW_2
+    ws = std::max(ws, pair_ws_floats(m, m.N, m.h, m.fr, EPI_NONE, m.fr, m.h, m.N));    // d_ln + dW_1
     ws = std::max(ws, gemm_ws_floats(m.dt, m.h, m.fr, m.N));       // dW_2
     ws = std::max(ws, gemm_ws_floats(m.dt, m.fr, m.h, m.N));       // dW_1
   }
@@ -130,22 +162,6 @@ P* slot(void* base, const Saved& s, int i) {
 // Row statistics [N][3] at the head of the xent statistics buffer, padded to 256 B.
 size_t xent_head_floats(int64_t rows) { return (size_t)((rows * 3 + 63) / 64) * 64; }
 
-GemmDesc gemm(const Dims& m, bool ak, bool bk, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-              const void* B, int64_t ldb, void* C, int64_t ldc) {
-  GemmDesc g{};
-  g.dtype = m.dt;
-  g.a_kmajor = ak;
-  g.b_kmajor = bk;
-  g.epi = EPI_NONE;
-  g.c_f32 = false;
-  g.M = M; g.N = N; g.K = K;
-  g.A = A; g.lda = lda;
-  g.B = B; g.ldb = ldb;
-  g.C = C; g.ldc = ldc;
-  g.C2 = nullptr; g.ldc2 = 0;
-  g.bias = nullptr;
-  return g;
-}
 
 // ------------------------------------------------------------------ tracing state
 
@@ -374,8 +390,9 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     gq.c_f32 = true;
     gq.ws = ws;
     const GemmDesc gqd = gemm(m, true, false, m.N, m.h, 3 * m.hr, dqkv, 3 * m.hr, p->w_in, m.h, d_ln_partial, m.h);
-    if (gemm_pair_wanted(gqd, gq)) {
-      TPL_TRY(launch_gemm_pair(gqd, gq, s));
+    PairPlan pq;
+    if (gemm_pair_plan(gqd, gq, &pq)) {
+      TPL_TRY(launch_gemm_pair(gqd, gq, pq, ws, s));
       TPL_TRY(launch_colsum(m.dt, dqkv, 3 * m.hr, m.N, 3 * m.hr, gr->d_b_in, ws, s));
     } else {
       TPL_TRY(launch_gemm(gq, s));
@@ -397,11 +414,12 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     g2.ws = ws;
     // the fc2 activation and weight gradients in one launch when that fills the
     // CUs better (the column partials then come in the paired tile's row blocks)
-    const bool pair2 = gemm_pair_wanted(g, g2);
+    PairPlan p2;
+    const bool pair2 = gemm_pair_plan(g, g2, &p2);
     const int64_t cp = pair2 ? gemm_pair_colpart_chunks(m.N) : gemm_colpart_chunks(m.dt, m.N, m.fr);
     if (cp > 0) g.colpart = ws;
     if (pair2) {
-      TPL_TRY(launch_gemm_pair(g, g2, s));
+      TPL_TRY(launch_gemm_pair(g, g2, p2, ws, s));
       if (cp > 0) TPL_TRY(launch_colsum_final(ws, cp, m.fr, gr->d_b_in, s));
     } else {
       TPL_TRY(launch_gemm(g, s));
@@ -412,8 +430,9 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     g1.c_f32 = true;
     g1.ws = ws;
     const GemmDesc g1d = gemm(m, true, false, m.N, m.h, m.fr, du, m.fr, p->w_in, m.h, d_ln_partial, m.h);
-    if (gemm_pair_wanted(g1d, g1)) {
-      TPL_TRY(launch_gemm_pair(g1d, g1, s));
+    PairPlan p1;
+    if (gemm_pair_plan(g1d, g1, &p1)) {
+      TPL_TRY(launch_gemm_pair(g1d, g1, p1, ws, s));
       if (cp == 0) TPL_TRY(launch_colsum(m.dt, du, m.fr, m.N, m.fr, gr->d_b_in, ws, s));
     } else {
       TPL_TRY(launch_gemm(g1, s));

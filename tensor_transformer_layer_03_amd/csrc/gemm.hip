@@ -1662,47 +1662,109 @@ int64_t gemm_colpart_chunks(int dtype, int64_t M, int64_t N) {
   const int rc = t.bm / (nt / t.bn);                                  // rows per partial block
   return (M + rc - 1) / rc;
 }
-// Pair a block's activation-gradient product dg (A K-major, B MN-major, bf16
-// out, EPI_NONE or EPI_DGELU) with its weight-gradient product wg (both
-// MN-major, fp32 out) in one launch when neither is split over K on its own
-// and list scheduling of both tile sets on the CUs (longer tiles first)
-// finishes at least 5% sooner than dg's own rounds plus wg perfectly packed
-// (what its tail split approaches). 175B rank: the MLP and QKV pairs, whose
-// activation gradients leave half or a quarter of the CUs idle in their last
-// round. TPL_GEMM_PAIR=0/1 forces the choice (tests).
-bool gemm_pair_wanted(const GemmDesc& dg, const GemmDesc& wg) {
-  if (dg.dtype != DT_BF16 || wg.dtype != DT_BF16) return false;
-  if (!dg.a_kmajor || dg.b_kmajor || dg.c_f32 || (dg.epi != EPI_NONE && dg.epi != EPI_DGELU)) return false;
-  if (wg.a_kmajor || wg.b_kmajor || !wg.c_f32 || wg.epi != EPI_NONE || wg.ldc != wg.N) return false;
-  if (dg.M <= 0 || dg.N <= 0 || dg.K <= 0 || wg.M <= 0 || wg.N <= 0 || wg.K <= 0) return false;
-  if (const char* f = getenv("TPL_GEMM_PAIR")) return f[0] == '1';
-  if (getenv("TPL_GEMM_TILE")) return false;
-  if (dg.epi == EPI_NONE && splitk_dgrad_for(dg.dtype, dg.M, dg.N, dg.K, ~size_t(0)).splits > 1) return false;
-  if (splitk_for(wg.dtype, wg.M, wg.N, wg.K).splits > 1) return false;
+// Pairing of a block's activation-gradient product dg (A K-major, B
+// MN-major, bf16 out, EPI_NONE or EPI_DGELU) with its weight-gradient product
+// wg (both MN-major, fp32 out, ldc == N) in one grid of 256x256 tiles. wg may
+// be split over K inside the grid (splits >= 1 write fp32 slices summed into
+// its output in split order afterwards). The plan takes the wg split whose
+// list schedule of both tile sets on the CUs (longer tiles first) ends
+// soonest, and is chosen when that beats the two products launched apart (dg
+// on its own rounds; wg split over K as it would be alone, else perfectly
+// packed, which its tail split approaches) by at least 5%. Times: a 256x256
+// tile of depth K takes 2*256*256*K flops at ~4.3 TFLOP/s per CU (the
+// measured per-CU rate of these kernels), and every split slice costs its
+// fp32 write and read back at ~5 TB/s. TPL_GEMM_PAIR=0/1 forces the choice
+// (tests). Workspace: dg's column partials (EPI_DGELU), then wg's slices.
+namespace {
+
+constexpr double kTileSecPerK = 2.0 * 256 * 256 / 4.3e12;
+constexpr double kSliceSecPerFloat = 8.0 / 5.0e12;
+
+PairPlan plan_pair(const GemmDesc& dg, const GemmDesc& wg, bool* wanted) {
+  PairPlan p{1, (int)wg.K};
+  *wanted = false;
+  if (dg.dtype != DT_BF16 || wg.dtype != DT_BF16) return p;
+  if (!dg.a_kmajor || dg.b_kmajor || dg.c_f32 || (dg.epi != EPI_NONE && dg.epi != EPI_DGELU)) return p;
+  if (wg.a_kmajor || wg.b_kmajor || !wg.c_f32 || wg.epi != EPI_NONE || wg.ldc != wg.N) return p;
+  if (dg.M <= 0 || dg.N <= 0 || dg.K <= 0 || wg.M <= 0 || wg.N <= 0 || wg.K <= 0) return p;
+  const char* force = getenv("TPL_GEMM_PAIR");
+  if (!force && getenv("TPL_GEMM_TILE")) return p;
   const int cus = device_cus();
   const int64_t td = ((dg.M + 255) / 256) * ((dg.N + 255) / 256), tw = ((wg.M + 255) / 256) * ((wg.N + 255) / 256);
-  int64_t groups[2][2] = {{td, dg.K}, {tw, wg.K}};
-  if (wg.K > dg.K) {
-    std::swap(groups[0][0], groups[1][0]);
-    std::swap(groups[0][1], groups[1][1]);
+  // the best split of wg inside the pair (each split at least 1024 deep)
+  double best = 0.0;
+  for (int sp = 1; sp <= 8; ++sp) {
+    if (sp > 1 && wg.K / sp < 1024) break;
+    const int64_t chunk = ((wg.K + sp - 1) / sp + 63) / 64 * 64;
+    const int nsp = (int)((wg.K + chunk - 1) / chunk);
+    if (nsp != sp) continue;
+    int64_t groups[2][2] = {{td, dg.K}, {tw * sp, chunk}};
+    if (chunk > dg.K) {
+      std::swap(groups[0][0], groups[1][0]);
+      std::swap(groups[0][1], groups[1][1]);
+    }
+    const double t = list_makespan(groups, 2, cus) * kTileSecPerK +
+                     (double)(sp - 1) * (double)wg.M * (double)wg.N * kSliceSecPerFloat;
+    if (sp == 1 || t < best) {
+      best = t;
+      p.wg_splits = sp;
+      p.wg_kchunk = (int)chunk;
+    }
   }
+  if (force) {
+    *wanted = force[0] == '1';
+    return p;
+  }
+  if (dg.epi == EPI_NONE && splitk_dgrad_for(dg.dtype, dg.M, dg.N, dg.K, ~size_t(0)).splits > 1) return p;
   const int64_t one[1][2] = {{td, dg.K}};
-  const double paired = list_makespan(groups, 2, cus);
-  const double apart = list_makespan(one, 1, cus) + (double)tw * (double)wg.K / cus;
-  return paired < 0.95 * apart;
+  double apart = list_makespan(one, 1, cus) * kTileSecPerK;
+  const SplitK sk = splitk_for(wg.dtype, wg.M, wg.N, wg.K);
+  if (sk.splits > 1) {
+    const int64_t tiles = sk.tile == 128 ? ((wg.M + 127) / 128) * ((wg.N + 127) / 128) : tw;
+    const int64_t w[1][2] = {{tiles * sk.splits, sk.kchunk}};
+    // a 128x128 workgroup has a quarter of the 256x256 work, two per CU
+    apart += (sk.tile == 128 ? list_makespan(w, 1, 2 * cus) / 4.0 * 2.0 : list_makespan(w, 1, cus)) * kTileSecPerK +
+             (double)(sk.splits - 1) * (double)wg.M * (double)wg.N * kSliceSecPerFloat;
+  } else {
+    apart += (double)tw * (double)wg.K / cus * kTileSecPerK;
+  }
+  *wanted = best < 0.95 * apart;
+  return p;
+}
+
+}  // namespace
+
+bool gemm_pair_plan(const GemmDesc& dg, const GemmDesc& wg, PairPlan* plan) {
+  bool wanted = false;
+  *plan = plan_pair(dg, wg, &wanted);
+  return wanted;
 }
 
 // Column-partial blocks the paired activation-gradient product writes for
 // EPI_DGELU (128 rows each: the 256x256 tile's eight waves as 4 x 2).
 int64_t gemm_pair_colpart_chunks(int64_t M) { return (M + 127) / 128; }
 
-hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, hipStream_t s) {
+size_t gemm_pair_ws_floats(const GemmDesc& dg, const GemmDesc& wg, const PairPlan& plan) {
+  const size_t cp = dg.epi == EPI_DGELU ? (size_t)gemm_pair_colpart_chunks(dg.M) * (size_t)dg.N : 0;
+  return (cp + 63) / 64 * 64 + (size_t)(plan.wg_splits - 1) * (size_t)wg.M * (size_t)wg.N;
+}
+
+hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, const PairPlan& plan, float* ws,
+                            hipStream_t s) {
   TraceScope trace(K_GEMM_PAIR, s, 2.0 * (double)dg.M * dg.N * dg.K + 2.0 * (double)wg.M * wg.N * wg.K);
-  if (dg.dtype != DT_BF16 || wg.dtype != DT_BF16) return hipErrorInvalidValue;
-  const Args a0 = pair_args(dg), a1 = pair_args(wg);
-  const int64_t t0 = (int64_t)a0.tiles_m * a0.tiles_n, t1 = (int64_t)a1.tiles_m * a1.tiles_n;
+  if (dg.dtype != DT_BF16 || wg.dtype != DT_BF16 || plan.wg_splits < 1) return hipErrorInvalidValue;
+  if (plan.wg_splits > 1 && !ws) return hipErrorInvalidValue;
+  Args a0 = pair_args(dg), a1 = pair_args(wg);
+  const size_t cp = dg.epi == EPI_DGELU ? (size_t)gemm_pair_colpart_chunks(dg.M) * (size_t)dg.N : 0;
+  a0.colpart = dg.epi == EPI_DGELU ? ws : nullptr;
+  if (plan.wg_splits > 1) {
+    a1.splits = plan.wg_splits;
+    a1.kchunk = plan.wg_kchunk;
+    a1.ws = ws + (cp + 63) / 64 * 64;
+  }
+  const int64_t t0 = (int64_t)a0.tiles_m * a0.tiles_n, t1 = (int64_t)a1.tiles_m * a1.tiles_n * a1.splits;
   if (t0 + t1 + 8 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  const bool wg_first = wg.K > dg.K;   // the longer tiles start first
+  const bool wg_first = a1.kchunk > dg.K;   // the longer tiles start first
   const int n0 = (int)(wg_first ? t1 : t0), n0pad = (n0 + 7) / 8 * 8, n1 = (int)(wg_first ? t0 : t1);
   if (n0 + n1 == 0) return hipSuccess;
   const dim3 grid((unsigned)(n0pad + n1)), block(512);
@@ -1721,6 +1783,11 @@ hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, hipStream_t 
       hipLaunchKernelGGL((gemm_pair_kernel<4, 2, true, false, EPI_NONE, bf16, 2, 4, false, false, EPI_NONE, float>),
                          grid, block, 0, s, a0, a1, n0, n0pad);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.wg_splits == 1) return e;
+  const int64_t quads = (wg.M * wg.N + 3) / 4;
+  hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
+                     static_cast<float*>(wg.C), wg.ldc, a1.ws, plan.wg_splits - 1, a1.M, a1.N);
   return hipGetLastError();
 }
 

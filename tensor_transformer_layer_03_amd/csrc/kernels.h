@@ -61,12 +61,17 @@ struct GemmDesc {
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
 // A block's activation-gradient product dg (A K-major, B MN-major, storage
 // type out, EPI_NONE or EPI_DGELU) and its weight-gradient product wg (both
-// MN-major, fp32 out, ldc == N) in one launch on 256x256 tiles, no split
-// over K; gemm_pair_wanted says when that beats two launches, and an
-// EPI_DGELU dg then writes gemm_pair_colpart_chunks(dg.M) column partials.
-bool gemm_pair_wanted(const GemmDesc& dg, const GemmDesc& wg);
+// MN-major, fp32 out, ldc == N) in one launch on 256x256 tiles, wg possibly
+// split over K inside it. gemm_pair_plan says whether that beats two
+// launches (and fills *plan either way); the launch then needs
+// gemm_pair_ws_floats of workspace: an EPI_DGELU dg's
+// gemm_pair_colpart_chunks(dg.M) column partials first (dg.colpart is
+// ignored: they go to ws), then wg's split slices.
+struct PairPlan { int wg_splits, wg_kchunk; };
+bool gemm_pair_plan(const GemmDesc& dg, const GemmDesc& wg, PairPlan* plan);
 int64_t gemm_pair_colpart_chunks(int64_t M);
-hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, hipStream_t s);
+size_t gemm_pair_ws_floats(const GemmDesc& dg, const GemmDesc& wg, const PairPlan& plan);
+hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, const PairPlan& plan, float* ws, hipStream_t s);
 // Floats of split-K workspace the product (M, N, K) with both operands MN-major
 // and an fp32 output takes (0: it is not split).
 size_t gemm_ws_floats(int dtype, int64_t M, int64_t N, int64_t K);
