@@ -298,12 +298,20 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave) void gemm_kernel(Args g)
 //    columns base+4q..base+4q+3 and lane j receives column base+j, rows
 //    k0..k0+3 -- four consecutive k of one output row/column, as the MFMA wants.
 //
-// Schedule of one K-tile (4 k16-steps, one barrier): the loads of tile kt+1
-// are issued during step 0, interleaved with its MFMAs; the fragments of step
-// s+1 are read during the MFMAs of step s; the barrier sits inside step 3
-// (after the wave's loads of tile kt+1 have landed), and the first fragments
-// of tile kt+1 are read while the rest of step 3's MFMAs run. The body is one
-// basic block: past the last tile the loads go to a zero-length buffer.
+// Schedule of one K-tile (4 k16-steps, one barrier): the fragments of step
+// s+1 are read during the MFMAs of step s; the barrier sits inside step 3,
+// and the first fragments of tile kt+1 are read while the rest of step 3's
+// MFMAs run. Loads run ahead of the MFMAs so that a tile's global latency
+// (HBM when the weights are not cached) is covered by more than one K-tile:
+//  * direct-to-LDS: each operand has a ring of 2 or 3 LDS stages; the loads
+//    of tile kt+S-1 of an operand with S stages are issued during step 0,
+//    and the barrier waits only for tile kt+1 (the deeper tiles stay in
+//    flight; loads return in issue order, so the deeper operand is issued
+//    last);
+//  * register-staged: tile kt+1, loaded into registers during tile kt-1, is
+//    written to its LDS stage during step 2 of tile kt, and the loads of tile
+//    kt+2 are issued right after, a whole K-tile ahead of their use.
+// Past the last tile the loads go to a zero-length buffer.
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((__vector_size__(8)));
@@ -407,9 +415,9 @@ struct TileReg {
   }
 };
 
-// Loads of K-tile KT_ of both operands (into stage S_ for the direct-to-LDS
-// path, into registers otherwise); past the last tile the buffers are
-// zero-length (nothing is read, zeros are produced).
+// Buffer arguments (base, bytes, scalar offset) of K-tile KT_ of A and of B;
+// past the last tile the buffers are zero-length (nothing is read, zeros are
+// produced).
 // K-major operands: the range ends at the last valid element of the tile's
 // last row (((rows - 1) * ld + K) elements from the first row's start), so
 // the reads of a ragged last K-tile stop at the operand's end also when a
@@ -426,16 +434,6 @@ struct TileReg {
                                : (int64_t)(g.K - (KT_) * 64) * g.ldb * 2)                                 \
                         : 0),                                                                            \
       (B_K ? (KT_) * 128 : 0)
-#define TPL_ISSUE_TILES(KT_, S_)                                   \
-  do {                                                             \
-    if constexpr (DMA) {                                           \
-      tA.issue(TPL_TILE_ARGS_A(KT_), (S_), wave);                  \
-      tB.issue(TPL_TILE_ARGS_B(KT_), (S_) + kBOff, wave);          \
-    } else {                                                       \
-      tA.load(TPL_TILE_ARGS_A(KT_));                               \
-      tB.load(TPL_TILE_ARGS_B(KT_));                               \
-    }                                                              \
-  } while (0)
 
 // Fragment of tile row r0 + lane%32, k-slots 8*(lane/32)..+7 of step st.
 template <int ROWS, bool KMAJ, bool PAD>
@@ -461,14 +459,15 @@ __device__ __forceinline__ void frag_v2(Frag8<bf16>& f, const char* tile, int r0
   }
 }
 
-// Fragments of step st for a wave's TM row tiles (A) and TN column tiles (B).
+// Fragments of step st for a wave's TM row tiles (A) and TN column tiles (B),
+// from an A and a B stage.
 template <int BM, int BN, bool A_K, bool B_K, bool PAD, int TM, int TN>
-__device__ __forceinline__ void read_frags(Frag8<bf16> (&fa)[TM], Frag8<bf16> (&fb)[TN], const char* stage, int st,
-                                           int arow, int brow, int lane) {
+__device__ __forceinline__ void read_frags2(Frag8<bf16> (&fa)[TM], Frag8<bf16> (&fb)[TN], const char* sa,
+                                            const char* sb, int st, int arow, int brow, int lane) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) frag_v2<BM, A_K, PAD>(fa[i], stage, arow + i * 32, st, lane);
+  for (int i = 0; i < TM; ++i) frag_v2<BM, A_K, PAD>(fa[i], sa, arow + i * 32, st, lane);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) frag_v2<BN, B_K, PAD>(fb[j], stage + tile_bytes<BM, PAD>(), brow + j * 32, st, lane);
+  for (int j = 0; j < TN; ++j) frag_v2<BN, B_K, PAD>(fb[j], sb, brow + j * 32, st, lane);
 }
 
 template <int TM, int TN>
@@ -590,9 +589,29 @@ struct CStage {
   }
 };
 
-// LDS of one workgroup of the two-stage kernel: two stages of an A and a B tile.
+// LDS stages of the A and B tiles. Direct-to-LDS forward tiles keep a third
+// stage of the weight operand (B) where the LDS holds it: its rows come from
+// HBM when the weights are not cached, the activations (A) usually from the
+// caches. 256x192: 2 + 3 stages, 141 KB (measured on the 175B rank's forward
+// products: 10% faster from cold caches, level from warm ones); 256x128: 3 +
+// 3 stages, 146 KB. The 256x256 and 128x128 tiles keep 2 + 2 (a third stage
+// does not fit, or would halve the workgroups per CU).
 template <int BM, int BN, bool DMA>
-constexpr int body_smem_bytes() { return 2 * (tile_bytes<BM, DMA>() + tile_bytes<BN, DMA>()); }
+constexpr int stages_a() { return DMA && BM == 256 && BN == 128 ? 3 : 2; }
+template <int BM, int BN, bool DMA>
+constexpr int stages_b() { return DMA && BM == 256 && (BN == 192 || BN == 128) ? 3 : 2; }
+// LDS of one workgroup of the two-stage kernel: the A stages, then the B stages.
+template <int BM, int BN, bool DMA>
+constexpr int body_smem_bytes() {
+  return stages_a<BM, BN, DMA>() * tile_bytes<BM, DMA>() + stages_b<BM, BN, DMA>() * tile_bytes<BN, DMA>();
+}
+
+// s_waitcnt with a vmcnt limit and lgkmcnt(0) (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
 
 // One output tile (workgroup number bid of the product's grid); smem holds
 // body_smem_bytes<BM, BN, DMA>() bytes.
@@ -600,8 +619,6 @@ template <int BM, int BN, int WGM, int WGN, bool A_K, bool B_K, bool DMA, int EP
 __device__ __forceinline__ void gemm_bf16_body(Args g, int bid, char* smem) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN, TM = WTM / 32, TN = WTN / 32;
-  constexpr int kBOff = tile_bytes<BM, DMA>();                 // B tile offset in a stage
-  constexpr int kStage = kBOff + tile_bytes<BN, DMA>();
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -661,43 +678,80 @@ __device__ __forceinline__ void gemm_bf16_body(Args g, int bid, char* smem) {
 
   const int KT = g.K / 64;                  // full K-tiles; a partial last tile is handled after the loop
   const int ktail = g.K & 63;
-  const int kt_all = KT + (ktail ? 1 : 0);
+  constexpr int SA = stages_a<BM, BN, DMA>(), SB = stages_b<BM, BN, DMA>();
+  static_assert(SA >= 2 && SB >= 2 && SA - SB <= 1 && SB - SA <= 1 && (DMA || (SA == 2 && SB == 2)),
+                "stage rings differ by at most one stage; register staging keeps two");
+  constexpr int kTA = tile_bytes<BM, DMA>(), kTB = tile_bytes<BN, DMA>();
+  // DMA loads of the deeper tiles that may stay in flight at a barrier
+  constexpr int kWait = DMA ? TileDma<BM, A_K, NW>::kInst * (SA - 2) + TileDma<BN, B_K, NW>::kInst * (SB - 2) : 0;
+  const auto stA = [&](int t) { return smem + (t % SA) * kTA; };
+  const auto stB = [&](int t) { return smem + SA * kTA + (t % SB) * kTB; };
+#define TPL_LOAD_A(T_) tA.load(TPL_TILE_ARGS_A(T_))
+#define TPL_LOAD_B(T_) tB.load(TPL_TILE_ARGS_B(T_))
+#define TPL_DMA_A(T_) tA.issue(TPL_TILE_ARGS_A(T_), stA(T_), wave)
+#define TPL_DMA_B(T_) tB.issue(TPL_TILE_ARGS_B(T_), stB(T_), wave)
 
-  TPL_ISSUE_TILES(0, smem);
-  if constexpr (!DMA) {
-    tA.store(smem);
-    tB.store(smem + kBOff);
+  if constexpr (DMA) {
+#pragma unroll
+    for (int t = 0; t < (SA > SB ? SA : SB) - 1; ++t) {
+      if (SA > SB) {   // the deeper ring's loads last
+        if (t <= SB - 2) TPL_DMA_B(t);
+        if (t <= SA - 2) TPL_DMA_A(t);
+      } else {
+        if (t <= SA - 2) TPL_DMA_A(t);
+        if (t <= SB - 2) TPL_DMA_B(t);
+      }
+    }
+    wait_vm_lgkm<kWait>();   // tile 0 has landed
+  } else {
+    TPL_LOAD_A(0);
+    TPL_LOAD_B(0);
+    tA.store(stA(0));
+    tB.store(stB(0));
+    TPL_LOAD_A(1);
+    TPL_LOAD_B(1);
+    wait_vm_lgkm<63>();      // this wave's LDS writes are done (tile 1 stays in flight)
   }
-  __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
-  read_frags<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], smem, 0, wm * WTM, wn * WTN, lane);
+  read_frags2<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], stA(0), stB(0), 0, wm * WTM, wn * WTN, lane);
 
   for (int kt = 0; kt < KT; ++kt) {
-    const char* cur = smem + (kt & 1) * kStage;
-    char* nxt = smem + ((kt + 1) & 1) * kStage;
+    const char* ca = stA(kt);
+    const char* cb = stB(kt);
     // step 0: fragments of step 1 (first, so no LDS write is ordered before
-    // them), then the loads of the next tile, around this step's MFMAs
-    read_frags<BM, BN, A_K, B_K, DMA, TM, TN>(fa[1], fb[1], cur, 1, wm * WTM, wn * WTN, lane);
-    TPL_ISSUE_TILES(kt + 1, nxt);
+    // them), then (direct-to-LDS) the loads of the tiles ahead, around this
+    // step's MFMAs
+    read_frags2<BM, BN, A_K, B_K, DMA, TM, TN>(fa[1], fb[1], ca, cb, 1, wm * WTM, wn * WTN, lane);
+    if constexpr (DMA) {
+      if (SA > SB) {
+        TPL_DMA_B(kt + SB - 1);
+        TPL_DMA_A(kt + SA - 1);
+      } else {
+        TPL_DMA_A(kt + SA - 1);
+        TPL_DMA_B(kt + SB - 1);
+      }
+    }
     mfma_tile<TM, TN>(acc, fa[0], fb[0]);
 #pragma unroll
     for (int x = 0; x < kMf; ++x) {
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
       if (x < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-      if (x < kVm) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+      if (DMA && x < kVm) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
     }
     // steps 1, 2
-    read_frags<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], cur, 2, wm * WTM, wn * WTN, lane);
+    read_frags2<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], ca, cb, 2, wm * WTM, wn * WTN, lane);
     mfma_tile<TM, TN>(acc, fa[1], fb[1]);
 #pragma unroll
     for (int x = 0; x < kMf; ++x) {
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
       if (x < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
     }
-    read_frags<BM, BN, A_K, B_K, DMA, TM, TN>(fa[1], fb[1], cur, 3, wm * WTM, wn * WTN, lane);
-    if constexpr (!DMA) {   // stage `nxt` is free since the last barrier
-      tA.store(nxt);
-      tB.store(nxt + kBOff);
+    read_frags2<BM, BN, A_K, B_K, DMA, TM, TN>(fa[1], fb[1], ca, cb, 3, wm * WTM, wn * WTN, lane);
+    if constexpr (!DMA) {   // stage kt+1 is free since the last barrier; then tile kt+2 into the registers
+      tA.store(stA(kt + 1));
+      tB.store(stB(kt + 1));
+      TPL_LOAD_A(kt + 2);
+      TPL_LOAD_B(kt + 2);
     }
     mfma_tile<TM, TN>(acc, fa[0], fb[0]);
 #pragma unroll
@@ -705,15 +759,18 @@ __device__ __forceinline__ void gemm_bf16_body(Args g, int bid, char* smem) {
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
       if (x < kRd) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
       if (!DMA && x < kVm) __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
+      if (!DMA && x < kVm) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
     }
     // step 3: a few MFMAs, then sync on the next tile, then its first fragments
     // are read while the remaining MFMAs of this step run
     constexpr int kHead = kMf / 4;
 #pragma unroll
     for (int x = 0; x < kHead; ++x) mfma_step(acc[x / TN][x % TN], fb[1][x % TN], fa[1][x / TN]);
-    __builtin_amdgcn_s_waitcnt(0);          // this wave's loads of tile kt+1 have landed, its reads are done
-    __builtin_amdgcn_s_barrier();            // ... and every other wave's
-    read_frags<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], nxt, 0, wm * WTM, wn * WTN, lane);
+    // tile kt+1 has landed in this wave's share (direct-to-LDS) or been written
+    // (registers), and its fragment reads are done; then every other wave's
+    wait_vm_lgkm<DMA ? kWait : 63>();
+    __builtin_amdgcn_s_barrier();
+    read_frags2<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], stA(kt + 1), stB(kt + 1), 0, wm * WTM, wn * WTN, lane);
 #pragma unroll
     for (int x = kHead; x < kMf; ++x) mfma_step(acc[x / TN][x % TN], fb[1][x % TN], fa[1][x / TN]);
 #pragma unroll
@@ -723,12 +780,12 @@ __device__ __forceinline__ void gemm_bf16_body(Args g, int bid, char* smem) {
     }
   }
   if (ktail) {
-    // partial last tile (its loads were issued by the last loop iteration, or
-    // by the prologue when K < 64): k-slots at or past K contribute zero
-    const char* cur = smem + (KT & 1) * kStage;
+    // partial last tile (in its stage since the last loop barrier, or the
+    // prologue's when K < 64): k-slots at or past K contribute zero
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      if (st > 0) read_frags<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], cur, st, wm * WTM, wn * WTN, lane);
+      if (st > 0)
+        read_frags2<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], stA(KT), stB(KT), st, wm * WTM, wn * WTN, lane);
       if (KT * 64 + 16 * st + 8 * (lane >> 5) >= g.K) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) zero_frag(fa[0][i]);
@@ -738,12 +795,16 @@ __device__ __forceinline__ void gemm_bf16_body(Args g, int bid, char* smem) {
       mfma_tile<TM, TN>(acc, fa[0], fb[0]);
     }
   }
-  (void)kt_all;
+  __builtin_amdgcn_s_waitcnt(0);   // no load past the last tile is still in flight
+#undef TPL_LOAD_A
+#undef TPL_LOAD_B
+#undef TPL_DMA_A
+#undef TPL_DMA_B
 
   // epilogue through LDS (the stages are free once every wave is past its
   // last fragment read); fp32 tiles that exceed the LDS go in row passes
   using Stage = CStage<TC, BN, NW * 64>;
-  constexpr int kCap = 2 * kStage / Stage::kRowBytes;   // rows the LDS holds
+  constexpr int kCap = body_smem_bytes<BM, BN, DMA>() / Stage::kRowBytes;   // rows the LDS holds
   constexpr int kRP = kCap >= BM ? BM : (kCap >= 128 ? 128 : (kCap >= 64 ? 64 : 32));
   static_assert(kRP >= WTM && BM % kRP == 0 && kRP % WTM == 0, "staging rows must hold whole wave tiles");
   // GeLU epilogue: round 0 stages GeLU'(u) and leaves GeLU(u) in the
