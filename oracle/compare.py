@@ -5,10 +5,10 @@ For each output tensor g (GPU) against r (oracle), with (rtol, atol) =
 "max relative error <= 1e-4 for fp32, <= 2e-2 with atol 1e-2 for bf16"), and
 u the storage format's unit roundoff (2^-24 fp32, 2^-8 bf16):
 
- 1. max relative error, normwise:  max|g - r| <= rtol * max|r| + atol * rms(r)
+ 1. max relative error, normwise:  max|g - r| <= rtol * max|r| + a
  2. relative Frobenius error:      ||g - r||_2 <= rtol * ||r||_2
  3. elementwise band, EVERY element (no out-of-band allowance):
-        |g - r| <= atol * rms(r) + rtol * |r| + u * M
+        |g - r| <= a + rtol * |r| + u * M
     where M >= |r| is the magnitude of the terms that form the element,
     computed by the oracle (oracle.magnitude): ||a_i|| ||b_j|| for a product
     (what a relative change u of its operand vectors can move it by), the
@@ -18,10 +18,11 @@ u the storage format's unit roundoff (2^-24 fp32, 2^-8 bf16):
     whose terms cancel carries their rounding, not its own. Without M
     (mags=None) the third term is 0.
 
-The absolute floor is relative to the tensor's RMS so the gate does not
-depend on each tensor's unit (a weight gradient summed over thousands of
-tokens is ~50 per entry, a loss gradient ~1/N per entry); for a unit-RMS
-tensor it is the stated 1e-2.
+The absolute floor is a = atol * min(1, rms(r)): the stated atol for a
+tensor of unit scale or larger, and proportionally less for a tensor whose
+entries are small (a loss gradient is ~1/N per entry, an attention partial
+~0.03), where a fixed 1e-2 would admit any error. It is never looser than
+the stated atol.
 
 The vocabulary shard's row statistics (m, se, tl) are compared as
 (m, m + ln se, tl): the pair (m, se) only fixes the shard's log-sum-exp
@@ -37,12 +38,18 @@ TOLERANCES = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-2)}
 UNIT_ROUNDOFF = {"f32": 2.0 ** -24, "bf16": 2.0 ** -8}
 
 
-def tolerance(ref, dtype: str, mag=None):
-    """Elementwise tolerance atol * rms(r) + rtol * |r| + u * M of gate 3."""
+def abs_floor(ref, dtype: str) -> float:
+    """Absolute floor a = atol * min(1, rms(r)) of gates 1 and 3."""
     r = np.asarray(ref, np.float64)
-    rtol, atol = TOLERANCES[dtype]
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
-    tol = atol * rms + rtol * np.abs(r)
+    return TOLERANCES[dtype][1] * min(1.0, rms)
+
+
+def tolerance(ref, dtype: str, mag=None):
+    """Elementwise tolerance a + rtol * |r| + u * M of gate 3."""
+    r = np.asarray(ref, np.float64)
+    rtol = TOLERANCES[dtype][0]
+    tol = abs_floor(r, dtype) + rtol * np.abs(r)
     if mag is not None:
         tol = tol + UNIT_ROUNDOFF[dtype] * np.asarray(mag, np.float64)
     return tol
@@ -53,7 +60,7 @@ def compare_tensor(got, ref, dtype: str, mag=None) -> dict:
     r = np.asarray(ref, np.float64)
     if g.shape != r.shape:
         return {"ok": False, "why": f"shape {g.shape} != {r.shape}"}
-    rtol, atol = TOLERANCES[dtype]
+    rtol = TOLERANCES[dtype][0]
     if r.size == 0:
         return {"ok": True, "n": 0}
     m = np.zeros_like(r) if mag is None else np.asarray(mag, np.float64)
@@ -68,7 +75,7 @@ def compare_tensor(got, ref, dtype: str, mag=None) -> dict:
     max_err = float(np.max(err)) if np.isfinite(err).all() else float("inf")
     fro_err = float(np.linalg.norm(np.nan_to_num(g - r, nan=np.inf)))
     fro_ref = float(np.linalg.norm(r))
-    ok_norm = max_err <= rtol * max_ref + atol * rms
+    ok_norm = max_err <= rtol * max_ref + abs_floor(r, dtype)
     ok_fro = fro_err <= rtol * fro_ref
     ok_band = not bad.any()
     return {

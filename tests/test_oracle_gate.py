@@ -1,7 +1,7 @@
 """Pins of the parity gate's rounding allowance (CPU only).
 
 oracle.magnitude gives, for every output of the pass, the magnitude M of
-the terms that form it; the bf16 gate admits |g - r| <= atol * rms(r) +
+the terms that form it; the bf16 gate admits |g - r| <= atol * min(1, rms(r)) +
 rtol * |r| + 2^-8 * M on every element. Pinned here:
 
 * each magnitude rule against a brute-force loop over the terms it names,
