@@ -25,6 +25,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;   // largest exp2-domain growth of a row max before O is rescaled
 
 struct Args {
   const char* qkv; int64_t ld_qkv;
@@ -719,9 +720,22 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kt][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m, mx);
-      const float mc = m_new == -INFINITY ? 0.f : m_new * c;
-      const float alpha = __builtin_amdgcn_exp2f(m * c - mc);
+      // The reference max m moves only when some row's max has grown past it
+      // by more than 2^kLazy in the exp2 domain (or on the first visible
+      // tile): softmax does not depend on the reference, the probabilities
+      // stay below 2^kLazy, and the rescale of O (D/2 multiplies per lane)
+      // is skipped on most tiles of a long row.
+      if (__any(mx != -INFINITY && (m == -INFINITY || (mx - m) * c > kLazy))) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        m = m_new;
+      }
+      const float mc = m == -INFINITY ? 0.f : m * c;
       float sum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -732,12 +746,7 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
           sum += p;
         }
       sum += __shfl_xor(sum, 32, kWave);
-      l = l * alpha + sum;
-      m = m_new;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      l += sum;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         Frag8<bf16> pf;
