@@ -59,9 +59,18 @@ def asan_runtime() -> str:
     raise RuntimeError("clang ASan runtime (libclang_rt.asan-x86_64.so) not found")
 
 
+# Per-source flags. The attention kernels keep their MFMA accumulators in
+# VGPRs: with the compiler's default the softmax rescale and the loop-carried
+# outputs were copied between AGPRs and VGPRs on every key tile (about 128
+# extra VALU moves per tile at head size 128), and the forward needed 340
+# registers instead of 252.
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, asan: bool = False) -> str:
     obj = os.path.join(BUILD_ASAN if asan else BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, *(ASAN_FLAGS if asan else []), "-x", "hip", "-c", src, "-o", obj]
+    extra = SOURCE_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc(), *FLAGS, *extra, *(ASAN_FLAGS if asan else []), "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -584,25 +584,41 @@ struct NatTile {
   static constexpr int kPer = (kTotal + NT - 1) / NT;
   u32x4 r[kPer];
   __device__ __forceinline__ static int phys(int row, int c) { return (c & ~7) | ((c ^ swz_a(row)) & 7); }
-  // rows [row0, row0+64) of a head's [rows][d] block (row stride ld); rows >= nrows read as 0
-  __device__ __forceinline__ void load(const bf16* base, int64_t ld, int row0, int nrows, int tid) {
+  // A thread's chunks of a tile, fixed over the loop: byte offset from the
+  // tile's first row (row stride ld elements) and LDS byte offset; voff < 0
+  // marks a slot past the tile.
+  struct Map {
+    int voff[kPer], loff[kPer];
+  };
+  __device__ __forceinline__ static Map map(int64_t ld, int tid) {
+    Map m;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int p = tid + i * NT;
       const int row = p / kLC, c = p % kLC;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (p < kTotal && row0 + row < nrows) v = ld16(base + (int64_t)(row0 + row) * ld + c * 8);
-      r[i] = v;
+      m.voff[i] = p < kTotal ? (int)(((int64_t)row * ld + c * 8) * 2) : -1;
+      m.loff[i] = row * kRowBytes + phys(row, c) * 16;
     }
+    return m;
   }
-  __device__ __forceinline__ void store(char* lds, int tid) const {
+  // rows [row0, row0+64) of a head's [rows][d] block at base (row stride ld),
+  // through a buffer resource from row row0 that ends at the last valid
+  // element of row nrows-1: rows past it read as 0
+  __device__ __forceinline__ void load(const Map& m, const bf16* base, int64_t ld, int row0, int nrows) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the buffer-resource type exists only in the device pass
+    const int64_t bytes = nrows > row0 ? ((int64_t)(nrows - 1 - row0) * ld + D) * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base + (int64_t)row0 * ld), (short)0,
+                                          bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int p = tid + i * NT;
-      if (p >= kTotal) break;
-      const int row = p / kLC, c = p % kLC;
-      st16(lds + row * kRowBytes + phys(row, c) * 16, r[i]);
-    }
+    for (int i = 0; i < kPer; ++i)
+      if (m.voff[i] >= 0) r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, m.voff[i], 0, 0);
+#endif
+  }
+  __device__ __forceinline__ void store(const Map& m, char* lds) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (m.voff[i] >= 0) st16(lds + m.loff[i], r[i]);
   }
   // 8 consecutive d-values (chunk c) of one row
   __device__ __forceinline__ static void row_frag(Frag8<bf16>& f, const char* lds, int row, int c) {
@@ -670,12 +686,13 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
   const int ntiles = (kv_end + BKV - 1) / BKV;
   const int nsteps = (ntiles + SPL - 1) / SPL;   // SPL key tiles per step, one per parity
   Tile kl[SPL], vl[SPL];
+  const typename Tile::Map mp = Tile::map(a.ld_qkv, tid);
 #pragma unroll
   for (int u = 0; u < SPL; ++u) {
-    kl[u].load(Kg, a.ld_qkv, u * BKV, s, tid);
-    vl[u].load(Vg, a.ld_qkv, u * BKV, s, tid);
-    kl[u].store(sK[0][u], tid);
-    vl[u].store(sV[0][u], tid);
+    kl[u].load(mp, Kg, a.ld_qkv, u * BKV, s);
+    vl[u].load(mp, Vg, a.ld_qkv, u * BKV, s);
+    kl[u].store(mp, sK[0][u]);
+    vl[u].store(mp, sV[0][u]);
   }
   __syncthreads();
 
@@ -685,8 +702,8 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
     if (more) {
 #pragma unroll
       for (int u = 0; u < SPL; ++u) {
-        kl[u].load(Kg, a.ld_qkv, ((t + 1) * SPL + u) * BKV, s, tid);
-        vl[u].load(Vg, a.ld_qkv, ((t + 1) * SPL + u) * BKV, s, tid);
+        kl[u].load(mp, Kg, a.ld_qkv, ((t + 1) * SPL + u) * BKV, s);
+        vl[u].load(mp, Vg, a.ld_qkv, ((t + 1) * SPL + u) * BKV, s);
       }
     }
     if (kv0 < kv_end && (!CAUSAL || kv0 <= q0w + 31)) {
@@ -762,8 +779,8 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
     if (more) {
 #pragma unroll
       for (int u = 0; u < SPL; ++u) {
-        kl[u].store(sK[cur ^ 1][u], tid);
-        vl[u].store(sV[cur ^ 1][u], tid);
+        kl[u].store(mp, sK[cur ^ 1][u]);
+        vl[u].store(mp, sV[cur ^ 1][u]);
       }
     }
     __syncthreads();
@@ -858,12 +875,13 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
   const int ntiles = (kv_end + BKV - 1) / BKV;
   const int nsteps = (ntiles + SPL - 1) / SPL;   // SPL key tiles per step, one per parity
   Tile kl[SPL], vl[SPL];
+  const typename Tile::Map mp = Tile::map(a.ld_qkv, tid);
 #pragma unroll
   for (int u = 0; u < SPL; ++u) {
-    kl[u].load(Kg, a.ld_qkv, u * BKV, s, tid);
-    vl[u].load(Vg, a.ld_qkv, u * BKV, s, tid);
-    kl[u].store(sK[0][u], tid);
-    vl[u].store(sV[0][u], tid);
+    kl[u].load(mp, Kg, a.ld_qkv, u * BKV, s);
+    vl[u].load(mp, Vg, a.ld_qkv, u * BKV, s);
+    kl[u].store(mp, sK[0][u]);
+    vl[u].store(mp, sV[0][u]);
   }
   __syncthreads();
 
@@ -873,8 +891,8 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
     if (more) {
 #pragma unroll
       for (int u = 0; u < SPL; ++u) {
-        kl[u].load(Kg, a.ld_qkv, ((t + 1) * SPL + u) * BKV, s, tid);
-        vl[u].load(Vg, a.ld_qkv, ((t + 1) * SPL + u) * BKV, s, tid);
+        kl[u].load(mp, Kg, a.ld_qkv, ((t + 1) * SPL + u) * BKV, s);
+        vl[u].load(mp, Vg, a.ld_qkv, ((t + 1) * SPL + u) * BKV, s);
       }
     }
     if (kv0 < kv_end && (!CAUSAL || kv0 <= q0w + 31)) {
@@ -922,8 +940,8 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
     if (more) {
 #pragma unroll
       for (int u = 0; u < SPL; ++u) {
-        kl[u].store(sK[cur ^ 1][u], tid);
-        vl[u].store(sV[cur ^ 1][u], tid);
+        kl[u].store(mp, sK[cur ^ 1][u]);
+        vl[u].store(mp, sV[cur ^ 1][u]);
       }
     }
     __syncthreads();
@@ -1013,13 +1031,14 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
       sDl[buf][u][j] = q < s ? a.delta[stat + q] : 0.f;
     }
   };
+  const typename Tile::Map mq = Tile::map(a.ld_qkv, tid), md = Tile::map(a.ld_ctx, tid);
   if (ntiles > 0) {
 #pragma unroll
     for (int u = 0; u < SPL; ++u) {
-      ql[u].load(Qg, a.ld_qkv, qs + u * BQ, s, tid);
-      dl[u].load(dOg, a.ld_ctx, qs + u * BQ, s, tid);
-      ql[u].store(sQ[0][u], tid);
-      dl[u].store(sdO[0][u], tid);
+      ql[u].load(mq, Qg, a.ld_qkv, qs + u * BQ, s);
+      dl[u].load(md, dOg, a.ld_ctx, qs + u * BQ, s);
+      ql[u].store(mq, sQ[0][u]);
+      dl[u].store(md, sdO[0][u]);
     }
     stage_stats(0, qs);
   }
@@ -1031,8 +1050,8 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
     if (more) {
 #pragma unroll
       for (int u = 0; u < SPL; ++u) {
-        ql[u].load(Qg, a.ld_qkv, qs + ((t + 1) * SPL + u) * BQ, s, tid);
-        dl[u].load(dOg, a.ld_ctx, qs + ((t + 1) * SPL + u) * BQ, s, tid);
+        ql[u].load(mq, Qg, a.ld_qkv, qs + ((t + 1) * SPL + u) * BQ, s);
+        dl[u].load(md, dOg, a.ld_ctx, qs + ((t + 1) * SPL + u) * BQ, s);
       }
     }
     if (q0 < s && (!CAUSAL || q0 + BQ - 1 >= k0w)) {
@@ -1094,8 +1113,8 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
     if (more) {
 #pragma unroll
       for (int u = 0; u < SPL; ++u) {
-        ql[u].store(sQ[cur ^ 1][u], tid);
-        dl[u].store(sdO[cur ^ 1][u], tid);
+        ql[u].store(mq, sQ[cur ^ 1][u]);
+        dl[u].store(md, sdO[cur ^ 1][u]);
       }
       stage_stats(cur ^ 1, qs + (t + 1) * SPL * BQ);
     }
