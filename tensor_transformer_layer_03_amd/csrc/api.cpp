@@ -41,7 +41,6 @@ tpl_status check_desc(const tpl_desc* d, Dims* out) {
   const int fr = d->ffn / d->tp, vr = d->vocab / d->tp;
   if (d->hidden % 8 || fr % 8 || vr % 8) return TPL_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 96 && d->head_dim != 128) return TPL_ERR_UNSUPPORTED;
-  if (d->dtype == TPL_F32 && d->head_dim != 64) return TPL_ERR_UNSUPPORTED;
   // LayerNorm caches a row in registers: at most 32 16-byte chunks per lane.
   if (d->hidden > 64 * 32 * (d->dtype == TPL_BF16 ? 8 : 4)) return TPL_ERR_UNSUPPORTED;
   const int64_t N = (int64_t)d->seq * d->micro_batch;

@@ -149,6 +149,13 @@ __device__ __forceinline__ void store_rows(T* base, int64_t ld, int row, const f
     }
 }
 
+// LDS buffers per tile of the generic backward kernels: two (the next tile
+// is stored while the current one is read) except for fp32 above head size
+// 64, whose double-buffered tiles would exceed the 160 KB of a workgroup;
+// with one buffer the store of the next tile waits for a barrier.
+template <typename T, int D>
+constexpr int bwd_buffers() { return sizeof(T) == 4 && D > 64 ? 1 : 2; }
+
 // ------------------------------------------------------------------ forward
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(Args a) {
@@ -311,11 +318,12 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(Args a) {
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(Args a) {
   constexpr int NT = 256, BQ = 128, BKV = 64;
+  constexpr int NB = bwd_buffers<T, D>();
   using KT = RowTile<T, D, BKV, NT>;
   using TT = TransTile<T, D, NT>;
-  __shared__ __attribute__((aligned(16))) T sK[2][BKV * KT::kLd];
-  __shared__ __attribute__((aligned(16))) T sV[2][BKV * KT::kLd];
-  __shared__ __attribute__((aligned(16))) T sKt[2][D * TT::kLd];
+  __shared__ __attribute__((aligned(16))) T sK[NB][BKV * KT::kLd];
+  __shared__ __attribute__((aligned(16))) T sV[NB][BKV * KT::kLd];
+  __shared__ __attribute__((aligned(16))) T sKt[NB][D * TT::kLd];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
   // 1-D grid dealt heaviest query tiles first over all heads (causal tiles
@@ -365,7 +373,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(Args a) {
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1, kv0 = t * BKV;
+    const int cur = NB == 1 ? 0 : t & 1, kv0 = t * BKV;
     const bool more = t + 1 < ntiles;
     if (more) {
       k_ld.load(Kg, a.ld_qkv, kv0 + BKV, s, tid);
@@ -409,9 +417,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(Args a) {
       }
     }
     if (more) {
-      k_ld.store(sK[cur ^ 1], tid);
-      v_ld.store(sV[cur ^ 1], tid);
-      kt_ld.store(sKt[cur ^ 1], tid);
+      if (NB == 1) __syncthreads();   // one buffer: every wave is past its reads of it
+      k_ld.store(sK[NB == 1 ? 0 : cur ^ 1], tid);
+      v_ld.store(sV[NB == 1 ? 0 : cur ^ 1], tid);
+      kt_ld.store(sKt[NB == 1 ? 0 : cur ^ 1], tid);
     }
     __syncthreads();
   }
@@ -425,14 +434,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(Args a) {
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(Args a) {
   constexpr int NT = 256, BKB = 128, BQ = 64;
+  constexpr int NB = bwd_buffers<T, D>();
   using RT = RowTile<T, D, BQ, NT>;
   using TT = TransTile<T, D, NT>;
-  __shared__ __attribute__((aligned(16))) T sQ[2][BQ * RT::kLd];
-  __shared__ __attribute__((aligned(16))) T sdO[2][BQ * RT::kLd];
-  __shared__ __attribute__((aligned(16))) T sQt[2][D * TT::kLd];
-  __shared__ __attribute__((aligned(16))) T sdOt[2][D * TT::kLd];
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
-  __shared__ __attribute__((aligned(16))) float sDl[2][BQ];
+  __shared__ __attribute__((aligned(16))) T sQ[NB][BQ * RT::kLd];
+  __shared__ __attribute__((aligned(16))) T sdO[NB][BQ * RT::kLd];
+  __shared__ __attribute__((aligned(16))) T sQt[NB][D * TT::kLd];
+  __shared__ __attribute__((aligned(16))) T sdOt[NB][D * TT::kLd];
+  __shared__ __attribute__((aligned(16))) float sL[NB][BQ];
+  __shared__ __attribute__((aligned(16))) float sDl[NB][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, grp = lane >> 5;
   // 1-D grid dealt heaviest key tiles (the first ones, under a causal mask) first over all heads
@@ -493,7 +503,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(Args a) {
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1, q0 = qs + t * BQ;
+    const int cur = NB == 1 ? 0 : t & 1, q0 = qs + t * BQ;
     const bool more = t + 1 < ntiles;
     if (more) load_tile(q0 + BQ);
     if (!CAUSAL || q0 + BQ - 1 >= k0w) {
@@ -542,7 +552,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(Args a) {
         }
       }
     }
-    if (more) store_tile(cur ^ 1, q0 + BQ);
+    if (more) {
+      if (NB == 1) __syncthreads();   // one buffer: every wave is past its reads of it
+      store_tile(NB == 1 ? 0 : cur ^ 1, q0 + BQ);
+    }
     __syncthreads();
   }
   if (my_k < s) {
@@ -1257,11 +1270,17 @@ hipError_t bwd_t(const AttnDesc& d, hipStream_t s) {
 
 }  // namespace
 
-// bf16: head_dim 64, 96, 128. fp32: head_dim 64 only (the fp32 backward's LDS
-// tiles for larger heads exceed the 160 KB of a workgroup).
+// Head sizes 64, 96 and 128 in both storage types.
 hipError_t launch_attn_fwd(const AttnDesc& d, hipStream_t s) {
   TraceScope trace(K_ATTN_FWD, s, 4.0 * attn_pairs(d) * d.head_dim);       // QK^T, PV
-  if (d.dtype == DT_F32) return d.head_dim == 64 ? fwd_t<float, 64>(d, s) : hipErrorInvalidValue;
+  if (d.dtype == DT_F32) {
+    switch (d.head_dim) {
+      case 64: return fwd_t<float, 64>(d, s);
+      case 96: return fwd_t<float, 96>(d, s);
+      case 128: return fwd_t<float, 128>(d, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (d.head_dim) {
     case 64: return fwd_t<bf16, 64>(d, s);
     case 96: return fwd_t<bf16, 96>(d, s);
@@ -1270,7 +1289,14 @@ hipError_t launch_attn_fwd(const AttnDesc& d, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 hipError_t launch_attn_bwd(const AttnDesc& d, hipStream_t s) {
-  if (d.dtype == DT_F32) return d.head_dim == 64 ? bwd_t<float, 64>(d, s) : hipErrorInvalidValue;
+  if (d.dtype == DT_F32) {
+    switch (d.head_dim) {
+      case 64: return bwd_t<float, 64>(d, s);
+      case 96: return bwd_t<float, 96>(d, s);
+      case 128: return bwd_t<float, 128>(d, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (d.head_dim) {
     case 64: return bwd_t<bf16, 64>(d, s);
     case 96: return bwd_t<bf16, 96>(d, s);

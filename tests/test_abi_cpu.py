@@ -48,7 +48,7 @@ def good_desc(**kw):
     ({"seq": 0}, B.TPL_ERR_INVALID_ARG),
     ({"causal": 2}, B.TPL_ERR_INVALID_ARG),
     ({"head_dim": 32, "heads": 32}, B.TPL_ERR_UNSUPPORTED),
-    ({"head_dim": 128, "heads": 8, "dtype": "f32"}, B.TPL_ERR_UNSUPPORTED),
+    ({"head_dim": 80, "heads": 16, "hidden": 1280}, B.TPL_ERR_UNSUPPORTED),
 ])
 def test_bad_descriptors_are_rejected(kw, status):
     d = good_desc(**kw)

@@ -32,6 +32,10 @@ SMALL = [
                       vocab=512, causal=True, sigma_w=0.05, index=53, name="small_bf16_d128"),
     synth.tiny_config("bf16", hidden=128, heads=2, head_dim=64, ffn=512, tp=1, seq=1, micro_batch=5,
                       vocab=64, causal=True, sigma_w=0.05, index=54, name="small_bf16_seq1"),
+    synth.tiny_config("f32", hidden=192, heads=2, head_dim=96, ffn=384, tp=2, seq=75, micro_batch=2,
+                      vocab=144, causal=False, sigma_w=0.05, index=59, name="small_f32_d96_bidir"),
+    synth.tiny_config("f32", hidden=256, heads=2, head_dim=128, ffn=512, tp=1, seq=130, micro_batch=1,
+                      vocab=128, causal=True, sigma_w=0.05, index=60, name="small_f32_d128"),
 ]
 
 
