@@ -911,7 +911,10 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
     if (kv0 < kv_end && (!CAUSAL || kv0 <= q0w + 31)) {
       const char* tK = sK[cur][par];
       const char* tV = sV[cur][par];
-      const bool mask = (CAUSAL && kv0 + BKV - 1 > q0w) || kv0 + BKV > s || my_q >= s;
+      // wave-uniform (q0w comes from the wave index): one scalar branch skips the
+      // masking of every score on tiles that need none (a per-lane flag would
+      // run the masking code under an exec mask for every score of every tile)
+      const bool mask = (CAUSAL && kv0 + BKV - 1 > q0w) || kv0 + BKV > s || q0w + 32 > s;
       // the tile's two 32-key halves one after the other (half the score
       // registers live at a time, so the accumulators stay in VGPRs)
 #pragma unroll
@@ -928,14 +931,16 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
           mfma_step(dp, vf, df[st]);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lse_q));
-          if (mask) {
+        for (int r = 0; r < 16; ++r) sc[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lse_q));
+        if (mask) {   // one scalar branch around the masking of the whole tile
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
             const int key = kv0 + 32 * kt + 16 * (r >> 3) + 8 * grp + (r & 7);
-            if (key >= s || (CAUSAL && key > my_q) || my_q >= s) p = 0.f;
+            if (key >= s || (CAUSAL && key > my_q) || my_q >= s) sc[r] = 0.f;
           }
-          sc[r] = p * (dp[r] - delta_q);   // dS^T
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = sc[r] * (dp[r] - delta_q);   // dS^T
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
           const int ks = 2 * kt + kh;
@@ -1072,7 +1077,8 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
       const char* tdO = sdO[cur][par];
       const float* tL = sL[cur][par];
       const float* tDl = sDl[cur][par];
-      const bool mask = (CAUSAL && q0 < k0w + 31) || q0 + BQ > s || my_k >= s;
+      // wave-uniform, as in the dQ kernel
+      const bool mask = (CAUSAL && q0 < k0w + 31) || q0 + BQ > s || k0w + 32 > s;
       // the tile's two 32-query halves one after the other (half the score
       // registers live at a time)
 #pragma unroll
@@ -1093,18 +1099,24 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
         for (int rq = 0; rq < 4; ++rq) {
           const int qo = qt * 32 + 16 * (rq >> 1) + 8 * grp + 4 * (rq & 1);
           const f32x4 lq = *reinterpret_cast<const f32x4*>(&tL[qo]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[4 * rq + e] = __builtin_amdgcn_exp2f(fmaf(sc[4 * rq + e], c, -lq[e]));
+        }
+        // masking in one pass behind one scalar branch (the per-element form
+        // left a branch around every score)
+        if (mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int q = q0 + qt * 32 + 16 * (r >> 3) + 8 * grp + (r & 7);
+            if (q >= s || my_k >= s || (CAUSAL && my_k > q)) sc[r] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int qo = qt * 32 + 16 * (rq >> 1) + 8 * grp + 4 * (rq & 1);
           const f32x4 dq = *reinterpret_cast<const f32x4*>(&tDl[qo]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rq + e;
-            float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lq[e]));
-            if (mask) {
-              const int q = q0 + qo + e;
-              if (q >= s || my_k >= s || (CAUSAL && my_k > q)) p = 0.f;
-            }
-            sc[r] = p;                       // P
-            dp[r] = p * (dp[r] - dq[e]);     // dS
-          }
+          for (int e = 0; e < 4; ++e) dp[4 * rq + e] = sc[4 * rq + e] * (dp[4 * rq + e] - dq[e]);   // dS
         }
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
