@@ -45,6 +45,7 @@ struct RowTile {
   static constexpr int kCpr = D / kVec;
   static constexpr int kTotal = ROWS * kCpr;
   static constexpr int kPer = (kTotal + NT - 1) / NT;
+  static_assert(NT % 64 == 0, "whole waves per workgroup");
   u32x4 r[kPer];
   // base points at element (row 0, col 0) of the head; rows >= nrows read as 0.
   __device__ __forceinline__ void load(const T* base, int64_t ld, int row0, int nrows, int tid) {
@@ -595,6 +596,7 @@ struct NatTile {
   static constexpr int kBytes = 64 * kRowBytes;
   static constexpr int kTotal = 64 * kLC;
   static constexpr int kPer = (kTotal + NT - 1) / NT;
+  static_assert(NT % 64 == 0, "whole waves per workgroup");
   u32x4 r[kPer];
   __device__ __forceinline__ static int phys(int row, int c) { return (c & ~7) | ((c ^ swz_a(row)) & 7); }
   // A thread's chunks of a tile, fixed over the loop: byte offset from the
@@ -625,13 +627,21 @@ struct NatTile {
                                           bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      if (m.voff[i] >= 0) r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, m.voff[i], 0, 0);
+      if (valid(m, i)) r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, m.voff[i], 0, 0);
 #endif
   }
   __device__ __forceinline__ void store(const Map& m, char* lds) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      if (m.voff[i] >= 0) st16(lds + m.loff[i], r[i]);
+      if (valid(m, i)) st16(lds + m.loff[i], r[i]);
+  }
+  // Slot i of a thread holds a chunk of the tile. kTotal is a multiple of 64
+  // and every wave's slots start at a multiple of 64, so a slot is valid for
+  // all lanes of a wave or for none: lane 0 decides (a scalar branch instead
+  // of an exec mask around every load and store).
+  __device__ __forceinline__ static bool valid(const Map& m, int i) {
+    if constexpr (kTotal % NT == 0) return true;
+    else return __builtin_amdgcn_readfirstlane(m.voff[i]) >= 0;
   }
   // 8 consecutive d-values (chunk c) of one row
   __device__ __forceinline__ static void row_frag(Frag8<bf16>& f, const char* lds, int row, int c) {

@@ -1379,6 +1379,24 @@ TailSplit tail_split_for(int64_t M, int64_t N, int64_t K, int cus) {
   return t;
 }
 
+// A weight-gradient product with between one and one and a half rounds of
+// 256x256 tiles would take three rounds of the 128x128 tile (two per CU,
+// relative per-CU throughput 0.8); the 256x256 tile with the tail split takes
+// its whole round plus the split tail rows (time of each in units of one
+// full-depth 256x256 round). Only for K >= 4096: measured on the 8.3B rank's
+// dE (300 tiles, K = 4096) 198 -> 182 us, but on the 175B rank's dW_o (288
+// tiles, K = 2048) 106 -> 110 us.
+bool tail_beats_128(int64_t M, int64_t N, int64_t K, const TailSplit& t, int cus) {
+  if (K < 4096) return false;
+  const int64_t tn = (N + 255) / 256, whole = (t.row0 / 256) * tn;
+  const int64_t tail = ((M - t.row0 + 255) / 256) * tn;
+  const double r256 = (double)((whole + cus - 1) / cus) +
+                      (double)((tail * t.splits + cus - 1) / cus) * (double)t.kchunk / (double)K;
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  const double r128 = (double)((t128 + 2 * cus - 1) / (2 * cus)) * (128.0 * 128.0 * 2.0 / 0.8) / 65536.0;
+  return r256 < r128;
+}
+
 // ------------------------------------------------------------------ dispatch
 
 struct TileCfg { int bm, bn, variant; };
@@ -1683,9 +1701,11 @@ hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     if constexpr (sizeof(T) == 2) {
       if (d.ws && splitk_for(d.dtype, d.M, d.N, d.K).tile == 256)
         return run_v2<256, 256, 2, 4, false, false, EPI_NONE, float>(d, s);
-      if (d.ldc == d.N && choose_tile(d.dtype, false, false, d.M, d.N).variant == 1) {
+      if (d.ldc == d.N) {
         const TailSplit t = tail_split_for(d.M, d.N, d.K, device_cus());
-        if (t.splits > 1) return run_tn_tail(d, t, s);
+        if (t.splits > 1 && (choose_tile(d.dtype, false, false, d.M, d.N).variant == 1 ||
+                             tail_beats_128(d.M, d.N, d.K, t, device_cus())))
+          return run_tn_tail(d, t, s);
       }
     }
     return run_tiles<T, false, false, EPI_NONE, float>(d, s);
