@@ -132,6 +132,7 @@ Saved saved_layout(const Dims& m, tpl_block block) {
     ws = std::max(ws, gemm_ws_floats(m.dt, 3 * m.hr, m.h, m.N));   // dW_qkv
     ws = std::max(ws, gemm_dgrad_ws_floats(m.dt, m.N, m.hr, m.h));  // dctx split over K
     ws = std::max(ws, pair_ws_floats(m, m.N, m.h, 3 * m.hr, EPI_NONE, 3 * m.hr, m.h, m.N));   // d_ln + dW_qkv
+    ws = std::max(ws, pair_ws_floats(m, m.N, m.hr, m.h, EPI_NONE, m.h, m.hr, m.N));           // dctx + dW_o
   } else {
     sz[S_GP] = m.N * m.fr * es;
     sz[S_ACT] = m.N * m.fr * es;
@@ -367,15 +368,21 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     void* dctx = slot<char>(saved, L, S_DCTX);
     void* dqkv = slot<char>(saved, L, S_DQKV);
     // dctx = dy W_o (split over K through the workspace when its grid is
-    // small: nothing else lives there yet) ; dW_o = dy^T ctx
+    // small: nothing else lives there yet) ; dW_o = dy^T ctx; the two in one
+    // launch when that fills the CUs better (both may then split over K)
     GemmDesc gd = gemm(m, true, false, m.N, m.hr, m.h, dy, m.h, p->w_out, m.hr, dctx, m.hr);
     gd.ws = ws;
     gd.ws_floats = (L.total - L.off[S_WS]) / 4;   // the workspace is the last slot
-    TPL_TRY(launch_gemm(gd, s));
     GemmDesc gw = gemm(m, false, false, m.h, m.hr, m.N, dy, m.h, ctx, m.hr, gr->d_w_out, m.hr);
     gw.c_f32 = true;
     gw.ws = ws;
-    TPL_TRY(launch_gemm(gw, s));
+    PairPlan po;
+    if (gemm_pair_plan(gd, gw, &po)) {
+      TPL_TRY(launch_gemm_pair(gd, gw, po, ws, s));
+    } else {
+      TPL_TRY(launch_gemm(gd, s));
+      TPL_TRY(launch_gemm(gw, s));
+    }
     AttnDesc a{};
     a.dtype = m.dt; a.batch = desc->micro_batch; a.heads = m.heads_r; a.seq = desc->seq;
     a.head_dim = m.d; a.causal = desc->causal;

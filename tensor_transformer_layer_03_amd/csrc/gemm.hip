@@ -1745,24 +1745,34 @@ int64_t gemm_colpart_chunks(int dtype, int64_t M, int64_t N) {
 }
 // Pairing of a block's activation-gradient product dg (A K-major, B
 // MN-major, bf16 out, EPI_NONE or EPI_DGELU) with its weight-gradient product
-// wg (both MN-major, fp32 out, ldc == N) in one grid of 256x256 tiles. wg may
-// be split over K inside the grid (splits >= 1 write fp32 slices summed into
-// its output in split order afterwards). The plan takes the wg split whose
-// list schedule of both tile sets on the CUs (longer tiles first) ends
-// soonest, and is chosen when that beats the two products launched apart (dg
-// on its own rounds; wg split over K as it would be alone, else perfectly
-// packed, which its tail split approaches) by at least 5%. Times: a 256x256
-// tile of depth K takes 2*256*256*K flops at ~4.3 TFLOP/s per CU (the
-// measured per-CU rate of these kernels), and every split slice costs its
-// fp32 write and read back at ~5 TB/s. TPL_GEMM_PAIR=0/1 forces the choice
-// (tests). Workspace: dg's column partials (EPI_DGELU), then wg's slices.
+// wg (both MN-major, fp32 out, ldc == N) in one grid of 256x256 tiles. Either
+// may be split over K inside the grid: wg's splits >= 1 write fp32 slices
+// summed into its output in split order afterwards; an EPI_NONE dg split
+// writes all its splits as fp32 slices, summed in split order and rounded
+// once into its output. The plan takes the pair of splits (each at least 1024
+// deep) whose list schedule of both tile sets on the CUs (longer tiles first)
+// ends soonest, and is chosen when that beats the two products launched
+// apart (each split over K as it would be alone; wg unsplit counted as
+// perfectly packed, which its tail split approaches). Times: a 256x256 tile
+// of depth K takes 2*256*256*K flops at ~4.3 TFLOP/s per CU (the measured
+// per-CU rate of these kernels), and every fp32 slice costs its write and read
+// back at ~5 TB/s. TPL_GEMM_PAIR=0/1 forces the choice (tests). Workspace:
+// dg's column partials (EPI_DGELU) or its split slices, then wg's slices.
 namespace {
 
 constexpr double kTileSecPerK = 2.0 * 256 * 256 / 4.3e12;
 constexpr double kSliceSecPerFloat = 8.0 / 5.0e12;
 
+// Splits of depth K each at least 1024 deep, as the kernels cut them
+// (chunk rounded up to 64); 0 when sp does not come out exactly.
+int64_t pair_chunk(int64_t K, int sp) {
+  if (sp > 1 && K / sp < 1024) return 0;
+  const int64_t chunk = ((K + sp - 1) / sp + 63) / 64 * 64;
+  return (K + chunk - 1) / chunk == sp ? chunk : 0;
+}
+
 PairPlan plan_pair(const GemmDesc& dg, const GemmDesc& wg, bool* wanted) {
-  PairPlan p{1, (int)wg.K};
+  PairPlan p{1, (int)dg.K, 1, (int)wg.K};
   *wanted = false;
   if (dg.dtype != DT_BF16 || wg.dtype != DT_BF16) return p;
   if (!dg.a_kmajor || dg.b_kmajor || dg.c_f32 || (dg.epi != EPI_NONE && dg.epi != EPI_DGELU)) return p;
@@ -1772,44 +1782,62 @@ PairPlan plan_pair(const GemmDesc& dg, const GemmDesc& wg, bool* wanted) {
   if (!force && getenv("TPL_GEMM_TILE")) return p;
   const int cus = device_cus();
   const int64_t td = ((dg.M + 255) / 256) * ((dg.N + 255) / 256), tw = ((wg.M + 255) / 256) * ((wg.N + 255) / 256);
-  // the best split of wg inside the pair (each split at least 1024 deep)
+  const double dmn = (double)dg.M * (double)dg.N, wmn = (double)wg.M * (double)wg.N;
   double best = 0.0;
-  for (int sp = 1; sp <= 8; ++sp) {
-    if (sp > 1 && wg.K / sp < 1024) break;
-    const int64_t chunk = ((wg.K + sp - 1) / sp + 63) / 64 * 64;
-    const int nsp = (int)((wg.K + chunk - 1) / chunk);
-    if (nsp != sp) continue;
-    int64_t groups[2][2] = {{td, dg.K}, {tw * sp, chunk}};
-    if (chunk > dg.K) {
-      std::swap(groups[0][0], groups[1][0]);
-      std::swap(groups[0][1], groups[1][1]);
-    }
-    const double t = list_makespan(groups, 2, cus) * kTileSecPerK +
-                     (double)(sp - 1) * (double)wg.M * (double)wg.N * kSliceSecPerFloat;
-    if (sp == 1 || t < best) {
-      best = t;
-      p.wg_splits = sp;
-      p.wg_kchunk = (int)chunk;
+  bool first = true;
+  for (int sd = 1; sd <= (dg.epi == EPI_NONE ? 8 : 1); ++sd) {
+    const int64_t cd = pair_chunk(dg.K, sd);
+    if (!cd) continue;
+    for (int sw = 1; sw <= 8; ++sw) {
+      const int64_t cw = pair_chunk(wg.K, sw);
+      if (!cw) continue;
+      int64_t groups[2][2] = {{td * sd, cd}, {tw * sw, cw}};
+      if (cw > cd) {
+        std::swap(groups[0][0], groups[1][0]);
+        std::swap(groups[0][1], groups[1][1]);
+      }
+      const double t = list_makespan(groups, 2, cus) * kTileSecPerK +
+                       (sd > 1 ? (double)sd * dmn * kSliceSecPerFloat : 0.0) +
+                       (double)(sw - 1) * wmn * kSliceSecPerFloat;
+      if (first || t < best) {
+        first = false;
+        best = t;
+        p = PairPlan{sd, (int)cd, sw, (int)cw};
+      }
     }
   }
   if (force) {
     *wanted = force[0] == '1';
     return p;
   }
-  if (dg.epi == EPI_NONE && splitk_dgrad_for(dg.dtype, dg.M, dg.N, dg.K, ~size_t(0)).splits > 1) return p;
-  const int64_t one[1][2] = {{td, dg.K}};
-  double apart = list_makespan(one, 1, cus) * kTileSecPerK;
+  // apart: dg on its own rounds (or its own split over K), then wg
+  double apart = 0.0;
+  const SplitK skd = dg.epi == EPI_NONE ? splitk_dgrad_for(dg.dtype, dg.M, dg.N, dg.K, ~size_t(0)) : SplitK{1, 0, 0};
+  // a 128x128 workgroup has a quarter of the 256x256 work, two per CU, at
+  // 0.8 of the 256x256 tile's per-CU rate (the tile cost model's figure)
+  auto split_time = [&](const SplitK& sk, int64_t M, int64_t N, int64_t t256) {
+    const int64_t tiles = sk.tile == 128 ? ((M + 127) / 128) * ((N + 127) / 128) : t256;
+    const int64_t w[1][2] = {{tiles * sk.splits, sk.kchunk}};
+    return (sk.tile == 128 ? list_makespan(w, 1, 2 * cus) / 4.0 * 2.0 / 0.8 : list_makespan(w, 1, cus)) * kTileSecPerK;
+  };
+  if (skd.splits > 1) {
+    apart += split_time(skd, dg.M, dg.N, td) + (double)skd.splits * dmn * kSliceSecPerFloat;
+  } else {
+    const int64_t one[1][2] = {{td, dg.K}};
+    apart += list_makespan(one, 1, cus) * kTileSecPerK;
+  }
   const SplitK sk = splitk_for(wg.dtype, wg.M, wg.N, wg.K);
   if (sk.splits > 1) {
-    const int64_t tiles = sk.tile == 128 ? ((wg.M + 127) / 128) * ((wg.N + 127) / 128) : tw;
-    const int64_t w[1][2] = {{tiles * sk.splits, sk.kchunk}};
-    // a 128x128 workgroup has a quarter of the 256x256 work, two per CU
-    apart += (sk.tile == 128 ? list_makespan(w, 1, 2 * cus) / 4.0 * 2.0 : list_makespan(w, 1, cus)) * kTileSecPerK +
-             (double)(sk.splits - 1) * (double)wg.M * (double)wg.N * kSliceSecPerFloat;
+    apart += split_time(sk, wg.M, wg.N, tw) + (double)(sk.splits - 1) * wmn * kSliceSecPerFloat;
+  } else if (choose_tile(wg.dtype, false, false, wg.M, wg.N).bm == 128) {
+    apart += split_time(SplitK{1, (int)wg.K, 128}, wg.M, wg.N, tw);
   } else {
     apart += (double)tw * (double)wg.K / cus * kTileSecPerK;
   }
-  *wanted = best < 0.95 * apart;
+  // measured: the pair wins even where the model puts it a few percent short
+  // of the two launches (8.3B rank fc1 backward, model 100.7 vs 104.7 us:
+  // 117.6 -> 107.1 us), so any modelled gain takes it
+  *wanted = best < apart;
   return p;
 }
 
@@ -1825,31 +1853,56 @@ bool gemm_pair_plan(const GemmDesc& dg, const GemmDesc& wg, PairPlan* plan) {
 // EPI_DGELU (128 rows each: the 256x256 tile's eight waves as 4 x 2).
 int64_t gemm_pair_colpart_chunks(int64_t M) { return (M + 127) / 128; }
 
+namespace {
+// Workspace of a pair: dg's column partials (EPI_DGELU) or split slices,
+// padded to 64 floats, then wg's slices.
+size_t pair_dg_floats(const GemmDesc& dg, const PairPlan& plan) {
+  size_t f = 0;
+  if (dg.epi == EPI_DGELU) f = (size_t)gemm_pair_colpart_chunks(dg.M) * (size_t)dg.N;
+  else if (plan.dg_splits > 1) f = (size_t)plan.dg_splits * (size_t)dg.M * (size_t)dg.N;
+  return (f + 63) / 64 * 64;
+}
+}  // namespace
+
 size_t gemm_pair_ws_floats(const GemmDesc& dg, const GemmDesc& wg, const PairPlan& plan) {
-  const size_t cp = dg.epi == EPI_DGELU ? (size_t)gemm_pair_colpart_chunks(dg.M) * (size_t)dg.N : 0;
-  return (cp + 63) / 64 * 64 + (size_t)(plan.wg_splits - 1) * (size_t)wg.M * (size_t)wg.N;
+  return pair_dg_floats(dg, plan) + (size_t)(plan.wg_splits - 1) * (size_t)wg.M * (size_t)wg.N;
 }
 
 hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, const PairPlan& plan, float* ws,
                             hipStream_t s) {
   TraceScope trace(K_GEMM_PAIR, s, 2.0 * (double)dg.M * dg.N * dg.K + 2.0 * (double)wg.M * wg.N * wg.K);
-  if (dg.dtype != DT_BF16 || wg.dtype != DT_BF16 || plan.wg_splits < 1) return hipErrorInvalidValue;
-  if (plan.wg_splits > 1 && !ws) return hipErrorInvalidValue;
+  if (dg.dtype != DT_BF16 || wg.dtype != DT_BF16 || plan.wg_splits < 1 || plan.dg_splits < 1) return hipErrorInvalidValue;
+  if (plan.dg_splits > 1 && dg.epi != EPI_NONE) return hipErrorInvalidValue;
+  if ((plan.wg_splits > 1 || plan.dg_splits > 1 || dg.epi == EPI_DGELU) && !ws) return hipErrorInvalidValue;
   Args a0 = pair_args(dg), a1 = pair_args(wg);
-  const size_t cp = dg.epi == EPI_DGELU ? (size_t)gemm_pair_colpart_chunks(dg.M) * (size_t)dg.N : 0;
   a0.colpart = dg.epi == EPI_DGELU ? ws : nullptr;
+  const bool dsplit = plan.dg_splits > 1;
+  if (dsplit) {   // every split of dg into fp32 slices: slice 0 at ws, slice s at ws + s*M*N
+    a0.C = reinterpret_cast<char*>(ws);
+    a0.ldc = dg.N;
+    a0.splits = plan.dg_splits;
+    a0.kchunk = plan.dg_kchunk;
+    a0.ws = ws + (int64_t)dg.M * dg.N;
+  }
   if (plan.wg_splits > 1) {
     a1.splits = plan.wg_splits;
     a1.kchunk = plan.wg_kchunk;
-    a1.ws = ws + (cp + 63) / 64 * 64;
+    a1.ws = ws + pair_dg_floats(dg, plan);
   }
-  const int64_t t0 = (int64_t)a0.tiles_m * a0.tiles_n, t1 = (int64_t)a1.tiles_m * a1.tiles_n * a1.splits;
+  const int64_t t0 = (int64_t)a0.tiles_m * a0.tiles_n * a0.splits, t1 = (int64_t)a1.tiles_m * a1.tiles_n * a1.splits;
   if (t0 + t1 + 8 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  const bool wg_first = a1.kchunk > dg.K;   // the longer tiles start first
+  const bool wg_first = a1.kchunk > a0.kchunk;   // the longer tiles start first
   const int n0 = (int)(wg_first ? t1 : t0), n0pad = (n0 + 7) / 8 * 8, n1 = (int)(wg_first ? t0 : t1);
   if (n0 + n1 == 0) return hipSuccess;
   const dim3 grid((unsigned)(n0pad + n1)), block(512);
-  if (wg_first) {
+  if (dsplit) {   // both products on the 2 x 4 wave layout with fp32 output
+    if (wg_first)
+      hipLaunchKernelGGL((gemm_pair_kernel<2, 4, false, false, EPI_NONE, float, 2, 4, true, false, EPI_NONE, float>),
+                         grid, block, 0, s, a1, a0, n0, n0pad);
+    else
+      hipLaunchKernelGGL((gemm_pair_kernel<2, 4, true, false, EPI_NONE, float, 2, 4, false, false, EPI_NONE, float>),
+                         grid, block, 0, s, a0, a1, n0, n0pad);
+  } else if (wg_first) {
     if (dg.epi == EPI_DGELU)
       hipLaunchKernelGGL((gemm_pair_kernel<2, 4, false, false, EPI_NONE, float, 4, 2, true, false, EPI_DGELU, bf16>),
                          grid, block, 0, s, a1, a0, n0, n0pad);
@@ -1865,7 +1918,14 @@ hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, const PairPl
                          grid, block, 0, s, a0, a1, n0, n0pad);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.wg_splits == 1) return e;
+  if (e != hipSuccess) return e;
+  if (dsplit) {
+    const int64_t quads = (dg.M * dg.N + 3) / 4;
+    hipLaunchKernelGGL(splitk_reduce_kernel<bf16>, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
+                       static_cast<bf16*>(dg.C), dg.ldc, ws, plan.dg_splits, a0.M, a0.N);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (plan.wg_splits == 1) return hipSuccess;
   const int64_t quads = (wg.M * wg.N + 3) / 4;
   hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
                      static_cast<float*>(wg.C), wg.ldc, a1.ws, plan.wg_splits - 1, a1.M, a1.N);
