@@ -1429,9 +1429,13 @@ hipError_t run(const GemmDesc& d, hipStream_t s) {
 // costs a whole one. Relative per-CU throughputs, fitted to timings of every
 // forward and gradient product of the four bf16 layer shards on MI355X:
 // 256x256 (8 waves, one workgroup per CU) 1.0; 256x192 (forward only) 0.8;
-// 128x128 (4 waves, two per CU) 0.7 forward, 0.8 gradient. (256x128 won some
-// gradient products timed alone but lost inside the layer pass, where the
-// operands arrive from the previous kernels instead of a warm cache.) The
+// 256x128 (forward only, 8 waves as 4 x 2) 0.75; 128x128 (4 waves, two per
+// CU) 0.7 forward, 0.8 gradient. (256x128 won some gradient products timed
+// alone but lost inside the layer pass, where the operands arrive from the
+// previous kernels instead of a warm cache. In the layer pass the model
+// gives it the forward products whose 256x256 grid is about half a round:
+// 8.3B rank fc1 (192 tiles) 68 -> 55 us and QKV 44 -> 42 us, GPT-2 fc2 (256
+// tiles) 79 -> 67 us and output projection 25 -> 24 us.) The
 // 256x256 tile runs as 2 x 4 waves of 128x64 for forward products and 4 x 2
 // waves of 64x128 for gradient products (faster there by up to 14% in the
 // same timings). Weight-gradient (TN) products keep 256x256 with 2 x 4 waves
@@ -1459,12 +1463,13 @@ TileCfg choose_tile(int dtype, bool ak, bool bk, int64_t M, int64_t N, int epi =
   struct Cand { TileCfg t; int per_cu; double thr; };
   const int64_t cus = device_cus();
   (void)epi;
-  Cand cands[3];
+  Cand cands[4];
   int nc = 0;
   if (nt) {
     cands[nc++] = {{256, 256, 1}, 1, 1.0};
     cands[nc++] = {{256, 192, 6}, 1, 0.8};
     cands[nc++] = {{128, 128, 0}, 2, 0.7};
+    cands[nc++] = {{256, 128, 4}, 1, 0.75};
   } else {
     cands[nc++] = {{256, 256, 2}, 1, 1.0};
     cands[nc++] = {{128, 128, 0}, 2, 0.8};
