@@ -160,17 +160,53 @@ __global__ __launch_bounds__(256) void ln_fwd_wide_kernel(const T* __restrict__ 
   if (tid == 0) { mu_out[row] = mean; rstd_out[row] = rstd; }
 }
 
+// Column sums finished inside another launch: out_k[c] = sum over chunks of
+// ws[chunk][k][c] (the partials of colpart_kernel). Workgroup b (four waves)
+// takes output k = b / ceil(cols / 64) and 64 consecutive columns (lane =
+// column); wave w adds chunks w, w + 4, ... in ascending order into four
+// accumulators, and the four wave sums are added in wave order: a fixed order.
+struct ColFinal {
+  const float* ws;
+  float* out[3];
+  int nchunks, nout, cols, nblk;   // nblk = 0: no column sums in this launch
+};
+constexpr int col_final_blocks(int nout, int cols) { return nout * ((cols + 63) / 64); }
+__device__ __forceinline__ void col_final(const ColFinal& f, int b) {
+  __shared__ float part[4][64];
+  const int per_out = (f.cols + 63) / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int k = b / per_out, c = (b % per_out) * 64 + lane;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  if (c < f.cols) {
+    const float* p = f.ws + (int64_t)k * f.cols + c;
+    const int64_t step = (int64_t)f.nout * f.cols;
+    int i = w;
+    for (; i + 12 < f.nchunks; i += 16) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] += p[(int64_t)(i + 4 * u) * step];
+    }
+    for (; i < f.nchunks; i += 4) a[0] += p[(int64_t)i * step];
+  }
+  part[w][lane] = (a[0] + a[1]) + (a[2] + a[3]);
+  __syncthreads();
+  if (w == 0 && c < f.cols) f.out[k][c] = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+}
+
 // dx = dy + rstd * (gd - mean(gd) - xhat * mean(gd * xhat)),  gd = dsum * gamma
 // (as ln_bwd_kernel below), one workgroup per row.
 template <typename T, int PER>
 __global__ __launch_bounds__(256) void ln_bwd_wide_kernel(const T* __restrict__ dy, const T* __restrict__ dsum,
                                                           const T* __restrict__ x, const float* __restrict__ mu,
                                                           const float* __restrict__ rstd, const T* __restrict__ g,
-                                                          T* __restrict__ dx, int cols) {
+                                                          T* __restrict__ dx, int cols, ColFinal f) {
   constexpr int V = Vec16<T>::N;
   __shared__ float red[2][4];
+  if ((int)blockIdx.x < f.nblk) {   // the first workgroups finish the column sums instead
+    col_final(f, (int)blockIdx.x);
+    return;
+  }
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  const int64_t row = (int64_t)blockIdx.x - f.nblk;
   const int nch = cols / V;
   const float m = mu[row], rs = rstd[row];
   u32x4 cd[PER], cx[PER], cy[PER];
@@ -628,11 +664,11 @@ hipError_t ln_fwd_wide_t(const void* x, const void* g, const void* b, void* y, f
 }
 template <typename T, int PER>
 hipError_t ln_bwd_wide_t(const void* dy, const void* dsum, const void* x, const float* mu, const float* rstd,
-                         const void* g, void* dx, int64_t rows, int cols, hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL((ln_bwd_wide_kernel<T, PER>), dim3((unsigned)rows), dim3(256), 0, s, static_cast<const T*>(dy),
-                     static_cast<const T*>(dsum), static_cast<const T*>(x), mu, rstd, static_cast<const T*>(g),
-                     static_cast<T*>(dx), cols);
+                         const void* g, void* dx, int64_t rows, int cols, const ColFinal& f, hipStream_t s) {
+  if (rows + f.nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL((ln_bwd_wide_kernel<T, PER>), dim3((unsigned)(rows + f.nblk)), dim3(256), 0, s,
+                     static_cast<const T*>(dy), static_cast<const T*>(dsum), static_cast<const T*>(x), mu, rstd,
+                     static_cast<const T*>(g), static_cast<T*>(dx), cols, f);
   return hipGetLastError();
 }
 
@@ -654,15 +690,19 @@ hipError_t launch_layernorm_fwd(int dtype, const void* x, const void* g, const v
   TPL_MAXC_SWITCH(mc, (ln_fwd_t<float, MC>(x, g, b, y, mu, rstd, rows, cols, eps, s)))
 }
 
+// Rows of the LayerNorm backward; on the wide-row path (one four-wave
+// workgroup per row) the same launch also finishes the column sums f.
 static hipError_t ln_bwd_rows(int dtype, const void* dy, const void* dsum, const void* x, const float* mu,
-                              const float* rstd, const void* g, void* dx, int64_t rows, int cols, hipStream_t s) {
+                              const float* rstd, const void* g, void* dx, int64_t rows, int cols, const ColFinal& f,
+                              hipStream_t s) {
   TraceScope trace(K_LN_BWD, s, (double)rows * cols * 4 * dtype_size(dtype) + rows * 8.0);
   const int mc = maxc_for(dtype, cols);
   if (mc > 2) {   // wide rows: one four-wave workgroup per row
     const int per = wide_per(dtype, cols);
-    if (dtype == DT_BF16) { TPL_PER_SWITCH(per, (ln_bwd_wide_t<bf16, PC>(dy, dsum, x, mu, rstd, g, dx, rows, cols, s))) }
-    TPL_PER_SWITCH(per, (ln_bwd_wide_t<float, PC>(dy, dsum, x, mu, rstd, g, dx, rows, cols, s)))
+    if (dtype == DT_BF16) { TPL_PER_SWITCH(per, (ln_bwd_wide_t<bf16, PC>(dy, dsum, x, mu, rstd, g, dx, rows, cols, f, s))) }
+    TPL_PER_SWITCH(per, (ln_bwd_wide_t<float, PC>(dy, dsum, x, mu, rstd, g, dx, rows, cols, f, s)))
   }
+  if (f.nblk) return hipErrorInvalidValue;   // column sums ride only on the wide-row launch
   if (dtype == DT_BF16) { TPL_MAXC_SWITCH(mc, (ln_bwd_t<bf16, MC>(dy, dsum, x, mu, rstd, g, dx, rows, cols, s))) }
   TPL_MAXC_SWITCH(mc, (ln_bwd_t<float, MC>(dy, dsum, x, mu, rstd, g, dx, rows, cols, s)))
 }
@@ -704,14 +744,19 @@ hipError_t launch_layernorm_bwd(int dtype, const void* dy, const void* dsum, con
                          rows, cols);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  {
+  ColFinal f{ws, {d_g, d_b, d_bout}, (int)n_chunks(rows), 3, cols, 0};
+  if (mc > 2) {
+    // wide rows: the rows launch finishes the column sums in its first
+    // workgroups (one launch fewer)
+    f.nblk = col_final_blocks(3, cols);
+  } else {
     TraceScope trace(K_COLSUM_FINAL, s);
     hipLaunchKernelGGL(colsum_final_kernel, dim3((cols + 63) / 64, 3), dim3(1024), 0, s, ws, (int)n_chunks(rows), cols,
                        3, d_g, d_b, d_bout);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // rows last: dx may alias dy (the residual path is read before it is overwritten per row)
-  return ln_bwd_rows(dtype, dy, dsum, x, mu, rstd, g, dx, rows, cols, s);
+  return ln_bwd_rows(dtype, dy, dsum, x, mu, rstd, g, dx, rows, cols, f, s);
 }
 
 hipError_t launch_colsum(int dtype, const void* X, int64_t ld, int64_t rows, int cols, float* out, float* ws,
