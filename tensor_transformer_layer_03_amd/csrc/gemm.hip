@@ -32,6 +32,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -1848,9 +1849,38 @@ PairPlan plan_pair(const GemmDesc& dg, const GemmDesc& wg, bool* wanted) {
 
 }  // namespace
 
+// Plans are memoized per (shapes, epilogue, CU count, forcing variables):
+// the search list-schedules up to 64 split pairs and costs up to ~0.25 ms of
+// host time, and every backward call asks for its plans twice (workspace
+// size, launch).
 bool gemm_pair_plan(const GemmDesc& dg, const GemmDesc& wg, PairPlan* plan) {
+  struct Key {
+    int64_t v[10];
+    bool operator==(const Key& o) const { return std::equal(v, v + 10, o.v); }
+  };
+  struct Entry { Key k; PairPlan p; bool wanted; };
+  static std::mutex mu;
+  static std::vector<Entry> memo;
+  const char* force = getenv("TPL_GEMM_PAIR");
+  const int64_t fk = force ? (force[0] == '1' ? 2 : 1) : (getenv("TPL_GEMM_TILE") ? 3 : 0);
+  const int64_t flags = (dg.a_kmajor ? 1 : 0) | (dg.b_kmajor ? 2 : 0) | (dg.c_f32 ? 4 : 0) | (wg.a_kmajor ? 8 : 0) |
+                        (wg.b_kmajor ? 16 : 0) | (wg.c_f32 ? 32 : 0) | (int64_t)(wg.ldc == wg.N) << 6 |
+                        (int64_t)dg.dtype << 8 | (int64_t)wg.dtype << 12 | (int64_t)dg.epi << 16 |
+                        (int64_t)wg.epi << 20 | fk << 24;
+  const Key k{{dg.M, dg.N, dg.K, wg.M, wg.N, wg.K, flags, (int64_t)device_cus(), 0, 0}};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& e : memo)
+      if (e.k == k) {
+        *plan = e.p;
+        return e.wanted;
+      }
+  }
   bool wanted = false;
   *plan = plan_pair(dg, wg, &wanted);
+  std::lock_guard<std::mutex> lock(mu);
+  if (memo.size() >= 256) memo.clear();
+  memo.push_back(Entry{k, *plan, wanted});
   return wanted;
 }
 
