@@ -147,9 +147,10 @@ def _tiny_inputs(cfg):
     return rep, shards, synth.oracle_params(cfg, shards, rep)
 
 
-def _torch_layer(cfg, p, x, targets, mask):
+def _torch_layer(cfg, p, x, targets, mask, with_loss=True):
     """Pre-LN transformer layer + output embedding + mean cross-entropy from
-    torch.nn library modules (fp64), independent of the oracle's code."""
+    torch.nn library modules (fp64), independent of the oracle's code
+    (with_loss=False: the layer only, loss None)."""
     h, a, s, b = cfg.hidden, cfg.heads, cfg.seq, cfg.micro_batch
     ln1, ln2 = torch.nn.LayerNorm(h, eps=cfg.ln_eps), torch.nn.LayerNorm(h, eps=cfg.ln_eps)
     mha = torch.nn.MultiheadAttention(h, a, bias=True, batch_first=True)
@@ -169,10 +170,12 @@ def _torch_layer(cfg, p, x, targets, mask):
     h1 = xt + mha(y, y, y, attn_mask=am, need_weights=False)[0]
     out = h1 + fc2(F.gelu(fc1(ln2(h1)), approximate="none"))
     out.retain_grad()
+    mods = dict(ln1=ln1, ln2=ln2, mha=mha, fc1=fc1, fc2=fc2, emb=emb)
+    if not with_loss:
+        return xt, out, None, mods
     logits = out.reshape(-1, h) @ emb.T
     rows = torch.tensor(np.nonzero(mask)[0])
     loss = F.cross_entropy(logits[rows], torch.tensor(targets, dtype=torch.long)[rows])
-    mods = dict(ln1=ln1, ln2=ln2, mha=mha, fc1=fc1, fc2=fc2, emb=emb)
     return xt, out, loss, mods
 
 
@@ -378,17 +381,30 @@ def test_local_stats_brute_force():
         assert st[i, 0] == m and abs(st[i, 1] - se) < 1e-13 and st[i, 2] == tl
 
 
-def test_flop_count_counts_visible_pairs():
-    for name in synth.CONFIG_ORDER:
-        cfg = synth.get_config(name)
-        f = O.layer_flops(cfg)
-        s = cfg.seq
-        mask = np.tril(np.ones((s, s))) if cfg.causal else np.ones((s, s))
-        pairs = int(mask.sum())
-        t, n, h = cfg.tp, cfg.rows, cfg.hidden
-        fwd = (2 * n * h * 3 * cfg.hidden_r + 4 * cfg.micro_batch * cfg.heads_r * pairs * cfg.head_dim
-               + 2 * n * cfg.hidden_r * h + 4 * n * h * cfg.ffn_r)
-        assert f["layer"] == 3 * fwd
+@pytest.mark.parametrize("causal", [False, True])
+def test_flop_count_matches_torch_counter(causal):
+    """layer_flops against counts it does not compute itself: torch's
+    FlopCounterMode over a forward + backward of the torch-module layer (it
+    counts the projection and MLP products, forward and both gradients; the
+    fused attention kernel is not counted), plus the attention products
+    counted per visible (query, key) pair by brute force: QK^T and PV each
+    2d flops per pair, three times for forward, dgrad and the other operand's
+    gradient."""
+    from torch.utils.flop_counter import FlopCounterMode
+    cfg = synth.tiny_config(causal=causal, mask_rows=None, seq=7, micro_batch=2, heads=2, head_dim=8, hidden=16,
+                            ffn=64, vocab=12, tp=1)
+    rep, shards, p = _tiny_inputs(cfg)
+    counter = FlopCounterMode(display=False)
+    with counter:
+        xt, out, _, _ = _torch_layer(cfg, p, rep.x, rep.targets, rep.mask, with_loss=False)
+        (out * T(rng(3).standard_normal(tuple(out.shape)))).sum().backward()
+    visible = sum(1 for i in range(cfg.seq) for j in range(cfg.seq) if not cfg.causal or j <= i)
+    attention = 3 * cfg.micro_batch * cfg.heads * visible * 2 * (2 * cfg.head_dim)
+    assert O.layer_flops(cfg)["layer"] == counter.get_total_flops() + attention
+
+
+def test_flop_count_of_the_gpt2_layer():
+    # the survey's figure for the GPT-2 355M layer (one TP rank of one)
     assert round(O.layer_flops(synth.get_config("gpt2_355m_t1"))["layer"] / 1e9, 1) == 670.1
 
 
