@@ -35,6 +35,10 @@
  *     exception: while enabled they keep process-wide state (an event pool
  *     and its records), create HIP events, and tpl_trace_read synchronises
  *     on the recorded events; the computation calls never depend on them.
+ *     Launch plans (tile shapes, splits over K, paired launches) are chosen
+ *     on the host from the shapes and the device's compute-unit count and
+ *     memoized per shape: the same call on the same device always launches
+ *     the same kernels, so results are bitwise repeatable.
  *   - Errors: arguments are validated on the host before anything is
  *     launched; a failed check returns TPL_ERR_INVALID_ARG (bad value, null or
  *     misaligned pointer) or TPL_ERR_UNSUPPORTED (valid but not implemented,
