@@ -717,6 +717,10 @@ __device__ __forceinline__ void gemm_bf16_body(Args g, int bid, char* smem) {
   read_frags2<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], stA(0), stB(0), 0, wm * WTM, wn * WTN, lane);
 
   for (int kt = 0; kt < KT; ++kt) {
+    // direct-to-LDS tiles: the wave's compute phase at raised issue priority,
+    // its wait for the next tile at the default (forward products 2-4%
+    // faster; level on the register-staged paths, which keep the default)
+    if constexpr (DMA) __builtin_amdgcn_s_setprio(1);
     const char* ca = stA(kt);
     const char* cb = stB(kt);
     // step 0: fragments of step 1 (first, so no LDS write is ordered before
@@ -769,6 +773,7 @@ __device__ __forceinline__ void gemm_bf16_body(Args g, int bid, char* smem) {
     for (int x = 0; x < kHead; ++x) mfma_step(acc[x / TN][x % TN], fb[1][x % TN], fa[1][x / TN]);
     // tile kt+1 has landed in this wave's share (direct-to-LDS) or been written
     // (registers), and its fragment reads are done; then every other wave's
+    if constexpr (DMA) __builtin_amdgcn_s_setprio(0);
     wait_vm_lgkm<DMA ? kWait : 63>();
     __builtin_amdgcn_s_barrier();
     read_frags2<BM, BN, A_K, B_K, DMA, TM, TN>(fa[0], fb[0], stA(kt + 1), stB(kt + 1), 0, wm * WTM, wn * WTN, lane);
