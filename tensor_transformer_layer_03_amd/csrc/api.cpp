@@ -131,7 +131,9 @@ Saved saved_layout(const Dims& m, tpl_block block) {
     ws = std::max(ws, gemm_ws_floats(m.dt, m.h, m.hr, m.N));       // dW_o
     ws = std::max(ws, gemm_ws_floats(m.dt, 3 * m.hr, m.h, m.N));   // dW_qkv
     ws = std::max(ws, gemm_dgrad_ws_floats(m.dt, m.N, m.hr, m.h));  // dctx split over K
-    ws = std::max(ws, pair_ws_floats(m, m.N, m.h, 3 * m.hr, EPI_NONE, 3 * m.hr, m.h, m.N));   // d_ln + dW_qkv
+    // d_ln + dW_qkv, then db_qkv's column partials past the pair's workspace
+    ws = std::max(ws, pair_ws_floats(m, m.N, m.h, 3 * m.hr, EPI_NONE, 3 * m.hr, m.h, m.N) +
+                          colsum_ws_floats(m.N, 3 * m.hr));
     ws = std::max(ws, pair_ws_floats(m, m.N, m.hr, m.h, EPI_NONE, m.h, m.hr, m.N));           // dctx + dW_o
   } else {
     sz[S_GP] = m.N * m.fr * es;
@@ -398,8 +400,18 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     const GemmDesc gqd = gemm(m, true, false, m.N, m.h, 3 * m.hr, dqkv, 3 * m.hr, p->w_in, m.h, d_ln_partial, m.h);
     PairPlan pq;
     if (gemm_pair_plan(gqd, gq, &pq)) {
-      TPL_TRY(launch_gemm_pair(gqd, gq, pq, ws, s));
-      TPL_TRY(launch_colsum(m.dt, dqkv, 3 * m.hr, m.N, 3 * m.hr, gr->d_b_in, ws, s));
+      if (pq.wg_splits > 1) {
+        // db_qkv's column partials in the launch that sums dW_qkv's split
+        // slices, into the workspace past the pair's own
+        float* wsc = ws + gemm_pair_ws_floats(gqd, gq, pq);
+        const PairTail t{TAIL_COLSUM_PARTIALS, dqkv, 3 * m.hr, m.N, 0, (int)(3 * m.hr), wsc, nullptr};
+        TPL_TRY(launch_gemm_pair(gqd, gq, pq, ws, s, &t));
+        const int64_t nch = (int64_t)(colsum_ws_floats(m.N, 3 * m.hr) / (size_t)(3 * m.hr));
+        TPL_TRY(launch_colsum_final(wsc, nch, 3 * m.hr, gr->d_b_in, s));
+      } else {
+        TPL_TRY(launch_gemm_pair(gqd, gq, pq, ws, s));
+        TPL_TRY(launch_colsum(m.dt, dqkv, 3 * m.hr, m.N, 3 * m.hr, gr->d_b_in, ws, s));
+      }
     } else {
       TPL_TRY(launch_gemm(gq, s));
       TPL_TRY(launch_colsum(m.dt, dqkv, 3 * m.hr, m.N, 3 * m.hr, gr->d_b_in, ws, s));
@@ -425,8 +437,12 @@ tpl_status tp_layer_shard_bwd(const tpl_desc* desc, tpl_block block, tpl_bwd_pha
     const int64_t cp = pair2 ? gemm_pair_colpart_chunks(m.N) : gemm_colpart_chunks(m.dt, m.N, m.fr);
     if (cp > 0) g.colpart = ws;
     if (pair2) {
-      TPL_TRY(launch_gemm_pair(g, g2, p2, ws, s));
-      if (cp > 0) TPL_TRY(launch_colsum_final(ws, cp, m.fr, gr->d_b_in, s));
+      // db_1's final column sum in the launch that sums dW_2's split slices
+      // when there is one
+      const bool merge = cp > 0 && p2.wg_splits > 1;
+      const PairTail t{TAIL_COLSUM_FINAL, nullptr, 0, 0, cp, (int)m.fr, ws, gr->d_b_in};
+      TPL_TRY(launch_gemm_pair(g, g2, p2, ws, s, merge ? &t : nullptr));
+      if (cp > 0 && !merge) TPL_TRY(launch_colsum_final(ws, cp, m.fr, gr->d_b_in, s));
     } else {
       TPL_TRY(launch_gemm(g, s));
       if (cp > 0) TPL_TRY(launch_colsum_final(ws, cp, m.fr, gr->d_b_in, s));

@@ -35,6 +35,7 @@
 #include <mutex>
 #include <vector>
 
+#include "colsum.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -1255,6 +1256,34 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(float* C, int64_t ldc, 
   *reinterpret_cast<f32x4*>(c) = acc;
 }
 
+// The split-slice sum of splitk_sum_kernel in workgroups [0, sum_blocks),
+// then the pair's column-sum tail (one role per workgroup).
+struct TailArgs {
+  int kind, nblk;
+  ColFinal f;
+  ColPartBf16 p;
+};
+__global__ __launch_bounds__(256) void splitk_sum_tail_kernel(float* C, int64_t ldc, const float* __restrict__ ws,
+                                                              int nsum, int M, int N, int sum_blocks, TailArgs t) {
+  if ((int)blockIdx.x < sum_blocks) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= (int64_t)M * N) return;
+    const int64_t m = i / N, n = i % N;
+    float* c = C + m * ldc + n;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(c);
+    for (int sp = 0; sp < nsum; ++sp) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(ws + (int64_t)sp * M * N + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += v[e];
+    }
+    *reinterpret_cast<f32x4*>(c) = acc;
+    return;
+  }
+  const int b = (int)blockIdx.x - sum_blocks;
+  if (t.kind == TAIL_COLSUM_FINAL) col_final(t.f, b);
+  else colpart_bf16_block(t.p, b);
+}
+
 struct SplitK { int splits, kchunk, tile; };
 
 // C[m][n] = ws[0][m][n] + ws[1][m][n] + ... in split order, stored as TC.
@@ -1909,7 +1938,7 @@ size_t gemm_pair_ws_floats(const GemmDesc& dg, const GemmDesc& wg, const PairPla
 }
 
 hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, const PairPlan& plan, float* ws,
-                            hipStream_t s) {
+                            hipStream_t s, const PairTail* tail) {
   TraceScope trace(K_GEMM_PAIR, s, 2.0 * (double)dg.M * dg.N * dg.K + 2.0 * (double)wg.M * wg.N * wg.K);
   if (dg.dtype != DT_BF16 || wg.dtype != DT_BF16 || plan.wg_splits < 1 || plan.dg_splits < 1) return hipErrorInvalidValue;
   if (plan.dg_splits > 1 && dg.epi != EPI_NONE) return hipErrorInvalidValue;
@@ -1965,10 +1994,23 @@ hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, const PairPl
                        static_cast<bf16*>(dg.C), dg.ldc, ws, plan.dg_splits, a0.M, a0.N);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (plan.wg_splits == 1) return hipSuccess;
-  const int64_t quads = (wg.M * wg.N + 3) / 4;
-  hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
-                     static_cast<float*>(wg.C), wg.ldc, a1.ws, plan.wg_splits - 1, a1.M, a1.N);
+  TailArgs t{};
+  t.kind = tail ? tail->kind : TAIL_NONE;
+  if (t.kind == TAIL_COLSUM_FINAL) {
+    t.f = ColFinal{tail->ws, {tail->out, nullptr, nullptr}, (int)tail->nchunks, 1, tail->cols, 0};
+    t.nblk = col_final_blocks(1, tail->cols);
+  } else if (t.kind == TAIL_COLSUM_PARTIALS) {
+    const int nbx = (tail->cols / 8 + 63) / 64;
+    t.p = ColPartBf16{static_cast<const bf16*>(tail->X), tail->ld, tail->rows, tail->cols, nbx, 0, tail->ws};
+    t.nblk = nbx * (int)((tail->rows + kRowsPerChunk - 1) / kRowsPerChunk);
+  } else if (t.kind != TAIL_NONE) {
+    return hipErrorInvalidValue;
+  }
+  const int64_t quads = plan.wg_splits > 1 ? (wg.M * wg.N + 3) / 4 : 0;
+  const int sum_blocks = (int)((quads + 255) / 256);
+  if (sum_blocks + t.nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(splitk_sum_tail_kernel, dim3((unsigned)(sum_blocks + t.nblk)), dim3(256), 0, s,
+                     static_cast<float*>(wg.C), wg.ldc, a1.ws, plan.wg_splits - 1, a1.M, a1.N, sum_blocks, t);
   return hipGetLastError();
 }
 

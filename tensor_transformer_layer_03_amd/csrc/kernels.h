@@ -71,7 +71,24 @@ struct PairPlan { int dg_splits, dg_kchunk, wg_splits, wg_kchunk; };
 bool gemm_pair_plan(const GemmDesc& dg, const GemmDesc& wg, PairPlan* plan);
 int64_t gemm_pair_colpart_chunks(int64_t M);
 size_t gemm_pair_ws_floats(const GemmDesc& dg, const GemmDesc& wg, const PairPlan& plan);
-hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, const PairPlan& plan, float* ws, hipStream_t s);
+// Column-sum work that launch_gemm_pair runs inside the launch summing wg's
+// split slices (a launch fewer), or in a launch of its own when there is no
+// such sum: TAIL_COLSUM_FINAL: out[c] = sum of the nchunks partial rows
+// ws[chunk][c] in chunk order; TAIL_COLSUM_PARTIALS: the per-32-row column
+// partials of the bf16 [rows][cols] operand X (row stride ld) into ws
+// ([ceil(rows/32)][cols], colsum_ws_floats). Its buffers must not overlap the
+// pair's workspace.
+enum { TAIL_NONE = 0, TAIL_COLSUM_FINAL = 1, TAIL_COLSUM_PARTIALS = 2 };
+struct PairTail {
+  int kind;
+  const void* X;
+  int64_t ld, rows, nchunks;
+  int cols;
+  float* ws;
+  float* out;
+};
+hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, const PairPlan& plan, float* ws, hipStream_t s,
+                            const PairTail* tail = nullptr);
 // Floats of split-K workspace the product (M, N, K) with both operands MN-major
 // and an fp32 output takes (0: it is not split).
 size_t gemm_ws_floats(int dtype, int64_t M, int64_t N, int64_t K);
