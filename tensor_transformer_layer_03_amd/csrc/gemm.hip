@@ -1256,17 +1256,37 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(float* C, int64_t ldc, 
   *reinterpret_cast<f32x4*>(c) = acc;
 }
 
-// The split-slice sum of splitk_sum_kernel in workgroups [0, sum_blocks),
-// then the pair's column-sum tail (one role per workgroup).
+// The work after a paired launch, one role per workgroup: a split
+// activation gradient's slices summed in split order and rounded to bf16
+// (workgroups [0, red_blocks)), the weight gradient's split slices added into
+// its output (the next sum_blocks), then the pair's column-sum tail.
 struct TailArgs {
   int kind, nblk;
   ColFinal f;
   ColPartBf16 p;
+  bf16* rc;             // split activation gradient: output, row stride, slices, count, shape
+  int64_t ldrc;
+  const float* rws;
+  int rsplits, rM, rN, red_blocks;
 };
 __global__ __launch_bounds__(256) void splitk_sum_tail_kernel(float* C, int64_t ldc, const float* __restrict__ ws,
                                                               int nsum, int M, int N, int sum_blocks, TailArgs t) {
-  if ((int)blockIdx.x < sum_blocks) {
+  if ((int)blockIdx.x < t.red_blocks) {
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= (int64_t)t.rM * t.rN) return;
+    const int64_t m = i / t.rN, n = i % t.rN;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(t.rws + i);
+    for (int sp = 1; sp < t.rsplits; ++sp) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(t.rws + (int64_t)sp * t.rM * t.rN + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += v[e];
+    }
+    store4(t.rc + m * t.ldrc + n, acc[0], acc[1], acc[2], acc[3]);
+    return;
+  }
+  const int bid = (int)blockIdx.x - t.red_blocks;
+  if (bid < sum_blocks) {
+    const int64_t i = ((int64_t)bid * 256 + threadIdx.x) * 4;
     if (i >= (int64_t)M * N) return;
     const int64_t m = i / N, n = i % N;
     float* c = C + m * ldc + n;
@@ -1279,7 +1299,7 @@ __global__ __launch_bounds__(256) void splitk_sum_tail_kernel(float* C, int64_t 
     *reinterpret_cast<f32x4*>(c) = acc;
     return;
   }
-  const int b = (int)blockIdx.x - sum_blocks;
+  const int b = bid - sum_blocks;
   if (t.kind == TAIL_COLSUM_FINAL) col_final(t.f, b);
   else colpart_bf16_block(t.p, b);
 }
@@ -1988,13 +2008,16 @@ hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, const PairPl
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (dsplit) {
-    const int64_t quads = (dg.M * dg.N + 3) / 4;
-    hipLaunchKernelGGL(splitk_reduce_kernel<bf16>, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
-                       static_cast<bf16*>(dg.C), dg.ldc, ws, plan.dg_splits, a0.M, a0.N);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   TailArgs t{};
+  if (dsplit) {   // dg's slices summed and rounded in the same launch as wg's sum and the tail
+    t.rc = static_cast<bf16*>(dg.C);
+    t.ldrc = dg.ldc;
+    t.rws = ws;
+    t.rsplits = plan.dg_splits;
+    t.rM = a0.M;
+    t.rN = a0.N;
+    t.red_blocks = (int)(((dg.M * dg.N + 3) / 4 + 255) / 256);
+  }
   t.kind = tail ? tail->kind : TAIL_NONE;
   if (t.kind == TAIL_COLSUM_FINAL) {
     t.f = ColFinal{tail->ws, {tail->out, nullptr, nullptr}, (int)tail->nchunks, 1, tail->cols, 0};
@@ -2008,8 +2031,8 @@ hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, const PairPl
   }
   const int64_t quads = plan.wg_splits > 1 ? (wg.M * wg.N + 3) / 4 : 0;
   const int sum_blocks = (int)((quads + 255) / 256);
-  if (sum_blocks + t.nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL(splitk_sum_tail_kernel, dim3((unsigned)(sum_blocks + t.nblk)), dim3(256), 0, s,
+  if (t.red_blocks + sum_blocks + t.nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(splitk_sum_tail_kernel, dim3((unsigned)(t.red_blocks + sum_blocks + t.nblk)), dim3(256), 0, s,
                      static_cast<float*>(wg.C), wg.ldc, a1.ws, plan.wg_splits - 1, a1.M, a1.N, sum_blocks, t);
   return hipGetLastError();
 }
