@@ -121,13 +121,23 @@ def test_attention_wave_forms(cfg, split, monkeypatch):
     _assert_ok(report)
 
 
+# 2200 rows, hidden 1152 (4.5 tiles of 256), ffn 2432 (9.5 tiles): deep enough over the
+# tokens that every paired weight gradient splits over K in two, the QKV and fc1 activation
+# gradients split too, so the launch after each pair runs its slice sums and its bias-gradient
+# column work (partials after the QKV pair, the final sum after the fc2 pair) on ragged tiles
+PAIR_SPLITS = synth.tiny_config("bf16", hidden=1152, heads=9, head_dim=128, ffn=2432, tp=1, seq=1100,
+                                micro_batch=2, vocab=256, causal=True, sigma_w=0.02, index=61,
+                                name="small_bf16_pair_splits")
+
+
 @pytest.mark.parametrize("pair", ["0", "1"])
-@pytest.mark.parametrize("cfg", [SMALL[1], SMALL[2], SMALL[3]], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [SMALL[1], SMALL[2], SMALL[3], PAIR_SPLITS], ids=lambda c: c.name)
 def test_paired_backward_products(cfg, pair, monkeypatch):
     """Each block's activation- and weight-gradient products in one launch
     (chosen automatically where it fills the CUs better, e.g. the 175B rank;
     forced on and off here on ragged shapes, with the fc2 pair's GeLU'
-    epilogue and bias-gradient column partials)."""
+    epilogue and bias-gradient column partials, and with splits over K and
+    the follow-on launch's sums on the deeper case)."""
     monkeypatch.setenv("TPL_GEMM_PAIR", pair)
     report, st = check_case(cfg)
     _assert_ok(report)
