@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (AMD data sheet)
 PEAK_HBM_GBS = 8000.0                           # MI355X HBM3E
-MFMA_KERNELS = {"gemm_nt", "gemm_nn", "gemm_tn", "gemm_pair", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"}
+MFMA_KERNELS = {"gemm_nt", "gemm_nn", "gemm_tn", "gemm_pair", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv",
+                "attn_bwd_pair"}
 METRIC = "TFLOP/s per TP layer-shard fwd+bwd (bf16) and % of MI355X MFMA peak"
 
 
@@ -281,7 +282,8 @@ def kernel_family(name: str) -> str:
         if "Li1E" in name or ", 1>" in name:
             return "colsum"
         return "colpart"
-    table = [("attn_bwd_dkdv", "attn_bwd_dkdv"), ("attn_bwd_dq", "attn_bwd_dq"), ("attn_bwd_pre", "attn_bwd_pre"),
+    table = [("attn_bwd_pair", "attn_bwd_pair"), ("attn_bwd_dkdv", "attn_bwd_dkdv"), ("attn_bwd_dq", "attn_bwd_dq"),
+             ("attn_bwd_pre", "attn_bwd_pre"),
              ("attn_fwd", "attn_fwd"), ("ln_bwd_cols", "layernorm_bwd_cols"), ("ln_bwd", "layernorm_bwd"),
              ("ln_fwd", "layernorm_fwd"), ("colsum_final", "colsum_final"), ("colsum", "colsum"),
              ("partial_sum", "partial_sum"), ("xent_stats", "xent_stats"), ("xent_finish", "xent_finish"),

@@ -176,7 +176,7 @@ const char* const kKernelNames[K_COUNT] = {
     "gemm_nt", "gemm_nn", "gemm_tn", "attn_fwd", "attn_bwd_pre", "attn_bwd_dq", "attn_bwd_dkdv",
     "layernorm_fwd", "layernorm_bwd", "layernorm_bwd_cols", "colsum", "colsum_final", "partial_sum",
     "xent_stats", "xent_finish", "xent_dlogits", "xent_merge", "embedding_fwd", "embedding_sort", "embedding_bwd",
-    "rows_gather", "rows_expand", "gemm_pair"};
+    "rows_gather", "rows_expand", "gemm_pair", "attn_bwd_pair"};
 
 }  // namespace
 

@@ -848,21 +848,28 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
 // KW waves of 32 queries per workgroup; SPL = 2: a second group of KW waves
 // takes every other key tile; the two partial dQ are added at the end (even
 // parity first). Forms as for the forward.
+template <int D, int SPL, int KW>
+struct DqLds {
+  using Tile = NatTile<D, 64 * KW * SPL>;
+  char sK[2][SPL][Tile::kBytes];
+  char sV[2][SPL][Tile::kBytes];
+};
+// The dQ kernel's work for query tile blk of a grid of nblk (heaviest first).
 template <int D, bool CAUSAL, int SPL, int KW>
-__global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(KW * SPL == 8 ? 2 : (D == 64 ? 3 : 1)))) void attn_bwd_dq_bf16_kernel(Args a) {
+__device__ __forceinline__ void attn_bwd_dq_bf16_body(const Args& a, DqLds<D, SPL, KW>& L, int blk, int nblk) {
   constexpr int NT = 64 * KW * SPL, BQ = 32 * KW, BKV = 64;
   constexpr int kLanes = 64 * KW;   // lanes of one parity group
   using Tile = NatTile<D, NT>;
-  __shared__ __attribute__((aligned(16))) char sK[2][SPL][Tile::kBytes];
-  __shared__ __attribute__((aligned(16))) char sV[2][SPL][Tile::kBytes];
+  auto& sK = L.sK;
+  auto& sV = L.sV;
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, grp = lane >> 5;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
   const int wave = wid % KW, par = wid / KW;                    // query sub-tile, key-tile parity
   // 1-D grid dealt heaviest query tiles first over all heads (causal tiles
   // differ up to seq/BQ-fold in work, so the last to start are the short ones)
-  const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs;
-  const int qb = gridDim.x / bhs - 1 - blockIdx.x / bhs;
+  const int bhs = a.batch * a.heads, bh = blk % bhs;
+  const int qb = nblk / bhs - 1 - blk / bhs;
   const int b = bh / a.heads, hd = bh % a.heads;
   const int s = a.seq, hr = a.heads * D;
   const bf16* Qg = reinterpret_cast<const bf16*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
@@ -997,6 +1004,11 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
     store_rows<bf16, D>(dQg, a.ld_qkv, my_q, dq, rsqrtf((float)D), grp);
   }
 }
+template <int D, bool CAUSAL, int SPL, int KW>
+__global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(KW * SPL == 8 ? 2 : (D == 64 ? 3 : 1)))) void attn_bwd_dq_bf16_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) DqLds<D, SPL, KW> L;
+  attn_bwd_dq_bf16_body<D, CAUSAL, SPL, KW>(a, L, (int)blockIdx.x, (int)gridDim.x);
+}
 
 // KW waves of 32 keys each per workgroup (BKB = 32 KW keys). SPL = 2: a
 // second group of KW waves takes every other query tile; the two partial dK
@@ -1004,20 +1016,30 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
 // default; (4, 2) for small grids at head size 64; (2, 2) for small grids at
 // 96 and 128, where two waves per SIMD would not fit the registers: twice the
 // workgroups of half the keys, one wave per SIMD.
+template <int D, int SPL, int KW>
+struct DkdvLds {
+  using Tile = NatTile<D, 64 * KW * SPL>;
+  char sQ[2][SPL][Tile::kBytes];
+  char sdO[2][SPL][Tile::kBytes];
+  float sL[2][SPL][64];
+  float sDl[2][SPL][64];
+};
+// The dK/dV kernel's work for key tile blk of a grid of nblk (heaviest first).
 template <int D, bool CAUSAL, int SPL, int KW>
-__global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(KW * SPL == 8 ? 2 : (D == 64 ? 2 : 1)))) void attn_bwd_dkdv_bf16_kernel(Args a) {
+__device__ __forceinline__ void attn_bwd_dkdv_bf16_body(const Args& a, DkdvLds<D, SPL, KW>& L, int blk, int nblk) {
   constexpr int NT = 64 * KW * SPL, BKB = 32 * KW, BQ = 64;
   using Tile = NatTile<D, NT>;
-  __shared__ __attribute__((aligned(16))) char sQ[2][SPL][Tile::kBytes];
-  __shared__ __attribute__((aligned(16))) char sdO[2][SPL][Tile::kBytes];
-  __shared__ __attribute__((aligned(16))) float sL[2][SPL][BQ];
-  __shared__ __attribute__((aligned(16))) float sDl[2][SPL][BQ];
+  auto& sQ = L.sQ;
+  auto& sdO = L.sdO;
+  auto& sL = L.sL;
+  auto& sDl = L.sDl;
+  (void)nblk;
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, grp = lane >> 5;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level branches stay scalar
   const int wave = wid % KW, par = wid / KW;                    // key sub-tile, query-tile parity
   // 1-D grid dealt heaviest key tiles (the first ones, under a causal mask) first over all heads
-  const int bhs = a.batch * a.heads, bh = blockIdx.x % bhs, kb = blockIdx.x / bhs;
+  const int bhs = a.batch * a.heads, bh = blk % bhs, kb = blk / bhs;
   const int b = bh / a.heads, hd = bh % a.heads;
   const int s = a.seq, hr = a.heads * D;
   const bf16* Qg = reinterpret_cast<const bf16*>(a.qkv) + (int64_t)b * s * a.ld_qkv + hd * D;
@@ -1188,6 +1210,37 @@ __global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(K
     store_rows<bf16, D>(dKg + hr, a.ld_qkv, my_k, dv, 1.f, grp);
   }
 }
+template <int D, bool CAUSAL, int SPL, int KW>
+__global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(KW * SPL == 8 ? 2 : (D == 64 ? 2 : 1)))) void attn_bwd_dkdv_bf16_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) DkdvLds<D, SPL, KW> L;
+  attn_bwd_dkdv_bf16_body<D, CAUSAL, SPL, KW>(a, L, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// dK/dV and dQ as the two roles of one grid (small grids): the two kernels
+// are independent (both read Q, K, V, dO and the row statistics; they write
+// dK/dV and dQ), and under a causal mask each leaves most CUs idle while its
+// heaviest tiles run. Workgroups alternate dK/dV, dQ in each role's own
+// heaviest-first order (the longer role's surplus last), so the light tiles of
+// one fill the CUs the other's heavy tiles leave; one LDS allocation serves
+// either role.
+template <int D, int SPL, int KW>
+union AttnBwdLds {
+  DkdvLds<D, SPL, KW> kv;
+  DqLds<D, SPL, KW> q;
+};
+template <int D, bool CAUSAL, int SPL, int KW>
+__global__ __launch_bounds__(64 * KW * SPL) __attribute__((amdgpu_waves_per_eu(KW * SPL == 8 ? 2 : 1))) void attn_bwd_pair_kernel(Args a, int n_kv, int n_q) {
+  __shared__ __attribute__((aligned(16))) AttnBwdLds<D, SPL, KW> L;
+  const int blk = (int)blockIdx.x, m = n_kv < n_q ? n_kv : n_q;
+  if (blk < 2 * m) {
+    if ((blk & 1) == 0) attn_bwd_dkdv_bf16_body<D, CAUSAL, SPL, KW>(a, L.kv, blk >> 1, n_kv);
+    else attn_bwd_dq_bf16_body<D, CAUSAL, SPL, KW>(a, L.q, blk >> 1, n_q);
+  } else if (n_kv > n_q) {
+    attn_bwd_dkdv_bf16_body<D, CAUSAL, SPL, KW>(a, L.kv, blk - m, n_kv);
+  } else {
+    attn_bwd_dq_bf16_body<D, CAUSAL, SPL, KW>(a, L.q, blk - m, n_q);
+  }
+}
 
 // Visible query-key pairs over all heads and sequences (causal: s(s+1)/2 each).
 double attn_pairs(const AttnDesc& d) {
@@ -1202,6 +1255,13 @@ bool attn_split(const AttnDesc& d) {
   if (const char* f = getenv("TPL_ATTN_SPLIT")) return atoi(f) != 0;
   const int64_t waves = (int64_t)((d.seq + 127) / 128) * d.batch * d.heads * 4;
   return waves < 2 * 4 * (int64_t)device_cu_count();
+}
+
+// dK/dV and dQ in one launch (attn_bwd_pair_kernel) when each role's n
+// workgroups fit one round; TPL_ATTN_BWD_PAIR=0/1 forces the choice (tests).
+bool attn_bwd_paired(int64_t n) {
+  if (const char* f = getenv("TPL_ATTN_BWD_PAIR")) return atoi(f) != 0;
+  return n <= (int64_t)device_cu_count();
 }
 
 Args make_args(const AttnDesc& d) {
@@ -1250,6 +1310,21 @@ hipError_t bwd_t(const AttnDesc& d, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   dim3 grid((unsigned)(((d.seq + 127) / 128) * d.batch * d.heads));
+  if constexpr (sizeof(T) == 2) {
+    // small grids whose dK/dV and dQ workgroups each fit one round on the
+    // CUs (one workgroup per CU: their LDS stages take over 64 KB): both as
+    // two roles of one launch (8.3B rank 54.6 -> 42.5 us; with 1.5 rounds
+    // each, as on the 175B rank, level, so those keep two launches)
+    constexpr int kKw = D == 64 ? 4 : 2;   // the small-grid forms of both kernels
+    const int64_t n = (int64_t)((d.seq + 32 * kKw - 1) / (32 * kKw)) * d.batch * d.heads;
+    if (attn_split(d) && attn_bwd_paired(n)) {
+      TraceScope trace(K_ATTN_BWD_PAIR, s, 8.0 * attn_pairs(d) * d.head_dim);   // dV, dP, dK; dQ's dP and dQ
+      const dim3 g((unsigned)(2 * n));
+      if (d.causal) hipLaunchKernelGGL((attn_bwd_pair_kernel<D, true, 2, kKw>), g, dim3(128 * kKw), 0, s, a, (int)n, (int)n);
+      else hipLaunchKernelGGL((attn_bwd_pair_kernel<D, false, 2, kKw>), g, dim3(128 * kKw), 0, s, a, (int)n, (int)n);
+      return hipGetLastError();
+    }
+  }
   {
     TraceScope trace(K_ATTN_BWD_DKDV, s, 6.0 * attn_pairs(d) * d.head_dim);   // dV, dP, dK
     if constexpr (sizeof(T) == 2) {

@@ -14,7 +14,7 @@ enum KernelId {
   K_GEMM_NT = 0, K_GEMM_NN, K_GEMM_TN, K_ATTN_FWD, K_ATTN_BWD_PRE, K_ATTN_BWD_DQ,
   K_ATTN_BWD_DKDV, K_LN_FWD, K_LN_BWD, K_LN_BWD_COLS, K_COLSUM, K_COLSUM_FINAL,
   K_PARTIAL_SUM, K_XENT_STATS, K_XENT_FINISH, K_XENT_DLOGITS, K_XENT_MERGE, K_EMB_FWD, K_EMB_SORT, K_EMB_BWD,
-  K_ROWS_GATHER, K_ROWS_EXPAND, K_GEMM_PAIR,
+  K_ROWS_GATHER, K_ROWS_EXPAND, K_GEMM_PAIR, K_ATTN_BWD_PAIR,
   K_COUNT
 };
 const char* kernel_name(int id);

@@ -52,6 +52,7 @@ def test_more_than_one_gpu_is_refused():
     ("tpl::(anonymous namespace)::splitk_sum_kernel(float*, long, float const*, int, int, int)", "gemm_tn"),
     ("void tpl::(anonymous namespace)::attn_bwd_dkdv_bf16_kernel<64, true, 1, 4>(tpl::(anonymous namespace)::Args)",
      "attn_bwd_dkdv"),
+    ("_ZN3tpl12_GLOBAL__N_120attn_bwd_pair_kernelILi96ELb1ELi2ELi2EEEvNS0_4ArgsEii", "attn_bwd_pair"),
     ("_ZN3tpl12_GLOBAL__N_119xent_dlogits_kernelIDF16bEEvPT_ilPKilPKhPKfS9_f", "xent_dlogits"),
     ("_ZN3tpl12_GLOBAL__N_118ln_fwd_wide_kernelIDF16bLi8EEEvPKT_S4_S4_PS2_PfS6_if", "layernorm_fwd"),
     ("tpl::(anonymous namespace)::embed_sort_lds_kernel(int const*, int, long, int, int, int, unsigned int*, unsig",

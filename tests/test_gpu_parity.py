@@ -110,13 +110,15 @@ def test_recompute_backward_matches_oracle(name, ranks):
     assert st.exchanges == 5
 
 
-@pytest.mark.parametrize("split", ["0", "1"])
+@pytest.mark.parametrize("split,bwd_pair", [("0", "0"), ("1", "0"), ("1", "1")])
 @pytest.mark.parametrize("cfg", [SMALL[1], SMALL[2], SMALL[3]], ids=lambda c: c.name)
-def test_attention_wave_forms(cfg, split, monkeypatch):
+def test_attention_wave_forms(cfg, split, bwd_pair, monkeypatch):
     """Both attention kernel forms on every head size: four waves per 128
     rows, and eight waves with the looped tiles dealt over two wave groups
-    (chosen automatically when the grid is small; forced here)."""
+    (chosen automatically when the grid is small; forced here), the latter's
+    backward as two launches or as the two roles of one launch."""
     monkeypatch.setenv("TPL_ATTN_SPLIT", split)
+    monkeypatch.setenv("TPL_ATTN_BWD_PAIR", bwd_pair)
     report, st = check_case(cfg)
     _assert_ok(report)
 
