@@ -136,6 +136,18 @@ def measure(st, steps, warmup, torch):
             "loss": kinds.get("loss", [0.0] * steps)}
 
 
+# A workload whose layer shard is under this many flops (the 8.3B rank's
+# 357.6 GF) runs about a millisecond a step, so its record times at least
+# SHORT_STEPS passes to keep the median's spread small.
+SHORT_LAYER_GFLOP = 400.0
+SHORT_STEPS = 50
+
+
+def sub_record_steps(cfg, steps: int) -> int:
+    """Timed passes for a workload's record: `steps`, or SHORT_STEPS for short ones."""
+    return max(steps, SHORT_STEPS) if step_flops(cfg, len(cfg.ranks()))["layer"] / 1e9 < SHORT_LAYER_GFLOP else steps
+
+
 def summary(cfg, n_ranks, m, peak):
     """Throughput figures of one workload from measure()'s per-step times."""
     fl = step_flops(cfg, n_ranks)
@@ -529,7 +541,9 @@ def main():
                 continue
             c2 = synth.get_config(name)
             s2, r2 = build_step(c2)
-            workloads[name] = summary(c2, len(r2), measure(s2, args.steps, args.warmup, torch), PEAK_TFLOPS[c2.dtype])
+            n2 = sub_record_steps(c2, args.steps)
+            workloads[name] = summary(c2, len(r2), measure(s2, n2, args.warmup, torch), PEAK_TFLOPS[c2.dtype])
+            workloads[name]["steps"] = n2
             del s2
             torch.cuda.empty_cache()
 
