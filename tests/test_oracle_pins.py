@@ -404,7 +404,8 @@ def test_flop_count_matches_torch_counter(causal):
 
 
 def test_flop_count_of_the_gpt2_layer():
-    # the survey's figure for the GPT-2 355M layer (one TP rank of one)
+    # 3 x forward flops of the GPT-2 355M layer at 8 x 1024 tokens (one TP rank of one), causal
+    # attention over visible pairs only: 670.1 GFLOP
     assert round(O.layer_flops(synth.get_config("gpt2_355m_t1"))["layer"] / 1e9, 1) == 670.1
 
 
