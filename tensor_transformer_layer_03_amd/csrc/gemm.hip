@@ -814,8 +814,8 @@ __device__ __forceinline__ void gemm_bf16_body(Args g, int bid, char* smem) {
   constexpr int kCap = body_smem_bytes<BM, BN, DMA>() / Stage::kRowBytes;   // rows the LDS holds
   constexpr int kRP = kCap >= BM ? BM : (kCap >= 128 ? 128 : (kCap >= 64 ? 64 : 32));
   static_assert(kRP >= WTM && BM % kRP == 0 && kRP % WTM == 0, "staging rows must hold whole wave tiles");
-  // GeLU epilogue: the first pass stages GeLU'(u) and leaves GeLU(u) in the
-  // accumulators, the second stages those
+  // GeLU epilogue: round 0 stages GeLU'(u) and leaves GeLU(u) in the
+  // accumulators, round 1 stages those
   constexpr int kRounds = EPI == EPI_BIAS_GELU ? 2 : 1;
   BiasCols<TN> bias;
   if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias.load(g.bias, g.N, n0 + wn * WTN, lane);
@@ -1198,8 +1198,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(
   // fragment read)
   using Stage = CStage<TC, BN, NW * 64>;
   static_assert(NS * kStage >= BM * Stage::kRowBytes, "the stages must hold the staged tile");
-  // GeLU epilogue: the first pass stages GeLU'(u) and leaves GeLU(u) in the
-  // accumulators, the second stages those
+  // GeLU epilogue: round 0 stages GeLU'(u) and leaves GeLU(u) in the
+  // accumulators, round 1 stages those
   constexpr int kRounds = EPI == EPI_BIAS_GELU ? 2 : 1;
   BiasCols<TN> bias;
   if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_GELU) bias.load(g.bias, g.N, n0 + wn * WTN, lane);
