@@ -913,6 +913,22 @@ __global__ __launch_bounds__(512) void gemm_pair_kernel(Args g0, Args g1, int n0
   }
 }
 
+// The same pairing on 128x128 tiles (four waves, 64 KB of LDS: two
+// workgroups per CU), for products whose widths are not multiples of 256 or
+// whose 256x256 grid is too coarse to balance; activation gradients without
+// an epilogue only.
+template <bool AK0, bool BK0, typename TC0, bool AK1, bool BK1, typename TC1>
+__global__ __launch_bounds__(256) void gemm_pair128_kernel(Args g0, Args g1, int n0, int n0pad) {
+  __shared__ __attribute__((aligned(1024))) char smem[body_smem_bytes<128, 128, false>()];
+  const int bid = blockIdx.x;
+  if (bid < n0pad) {
+    if (bid >= n0) return;
+    gemm_bf16_body<128, 128, 2, 2, AK0, BK0, false, EPI_NONE, TC0>(g0, bid, smem);
+  } else {
+    gemm_bf16_body<128, 128, 2, 2, AK1, BK1, false, EPI_NONE, TC1>(g1, bid - n0pad, smem);
+  }
+}
+
 // The same product as the first pass of a tail split (the last tile rows
 // split over K into fp32 partials); a symbol of its own so that a kernel
 // trace tells the two passes apart.
@@ -1690,7 +1706,7 @@ hipError_t run_tn_tail(const GemmDesc& d, const TailSplit& t, hipStream_t s) {
 }
 
 // Arguments of one product of a paired launch (256x256 tiles, no split).
-Args pair_args(const GemmDesc& d) {
+Args pair_args(const GemmDesc& d, int tile = 256) {
   Args a{};
   a.A = static_cast<const char*>(d.A); a.lda = d.lda;
   a.B = static_cast<const char*>(d.B); a.ldb = d.ldb;
@@ -1698,8 +1714,8 @@ Args pair_args(const GemmDesc& d) {
   a.C2 = static_cast<char*>(d.C2); a.ldc2 = d.ldc2;
   a.bias = static_cast<const char*>(d.bias);
   a.M = (int)d.M; a.N = (int)d.N; a.K = (int)d.K;
-  a.tiles_m = (a.M + 255) / 256;
-  a.tiles_n = (a.N + 255) / 256;
+  a.tiles_m = (a.M + tile - 1) / tile;
+  a.tiles_n = (a.N + tile - 1) / tile;
   a.splits = 1;
   a.kchunk = a.K;
   a.ws = nullptr;
@@ -1805,7 +1821,8 @@ int64_t gemm_colpart_chunks(int dtype, int64_t M, int64_t N) {
 }
 // Pairing of a block's activation-gradient product dg (A K-major, B
 // MN-major, bf16 out, EPI_NONE or EPI_DGELU) with its weight-gradient product
-// wg (both MN-major, fp32 out, ldc == N) in one grid of 256x256 tiles. Either
+// wg (both MN-major, fp32 out, ldc == N) in one grid of 256x256 tiles (or,
+// for a dg without an epilogue, 128x128 tiles where that schedules better). Either
 // may be split over K inside the grid: wg's splits >= 1 write fp32 slices
 // summed into its output in split order afterwards; an EPI_NONE dg split
 // writes all its splits as fp32 slices, summed in split order and rounded
@@ -1816,7 +1833,8 @@ int64_t gemm_colpart_chunks(int dtype, int64_t M, int64_t N) {
 // perfectly packed, which its tail split approaches). Times: a 256x256 tile
 // of depth K takes 2*256*256*K flops at ~4.3 TFLOP/s per CU (the measured
 // per-CU rate of these kernels), and every fp32 slice costs its write and read
-// back at ~5 TB/s. TPL_GEMM_PAIR=0/1 forces the choice (tests). Workspace:
+// back at ~5 TB/s. TPL_GEMM_PAIR=0/1 forces the choice and
+// TPL_GEMM_PAIR_TILE=256/128 the tile (tests). Workspace:
 // dg's column partials (EPI_DGELU) or its split slices, then wg's slices.
 namespace {
 
@@ -1864,6 +1882,43 @@ PairPlan plan_pair(const GemmDesc& dg, const GemmDesc& wg, bool* wanted) {
         best = t;
         p = PairPlan{sd, (int)cd, sw, (int)cw};
       }
+    }
+  }
+  // the same search on 128x128 tiles (activation gradients without an
+  // epilogue): two workgroups per CU, each at 0.8 of the 256x256 tile's
+  // per-CU rate, so a 128x128 tile of depth K takes 0.625 K units on one of
+  // 2 * cus slots
+  const char* ft = getenv("TPL_GEMM_PAIR_TILE");
+  const int tile_force = ft ? atoi(ft) : 0;
+  if (dg.epi == EPI_NONE && tile_force != 256) {
+    const int64_t td1 = ((dg.M + 127) / 128) * ((dg.N + 127) / 128), tw1 = ((wg.M + 127) / 128) * ((wg.N + 127) / 128);
+    bool first1 = true;
+    double best1 = 0.0;
+    PairPlan p1 = p;
+    for (int sd = 1; sd <= 8; ++sd) {
+      const int64_t cd = pair_chunk(dg.K, sd);
+      if (!cd) continue;
+      for (int sw = 1; sw <= 8; ++sw) {
+        const int64_t cw = pair_chunk(wg.K, sw);
+        if (!cw) continue;
+        int64_t groups[2][2] = {{td1 * sd, cd}, {tw1 * sw, cw}};
+        if (cw > cd) {
+          std::swap(groups[0][0], groups[1][0]);
+          std::swap(groups[0][1], groups[1][1]);
+        }
+        const double t = list_makespan(groups, 2, 2 * cus) * 0.625 * kTileSecPerK +
+                         (sd > 1 ? (double)sd * dmn * kSliceSecPerFloat : 0.0) +
+                         (double)(sw - 1) * wmn * kSliceSecPerFloat;
+        if (first1 || t < best1) {
+          first1 = false;
+          best1 = t;
+          p1 = PairPlan{sd, (int)cd, sw, (int)cw, 128};
+        }
+      }
+    }
+    if (!first1 && (tile_force == 128 || best1 < best)) {
+      best = best1;
+      p = p1;
     }
   }
   if (force) {
@@ -1916,7 +1971,9 @@ bool gemm_pair_plan(const GemmDesc& dg, const GemmDesc& wg, PairPlan* plan) {
   static std::mutex mu;
   static std::vector<Entry> memo;
   const char* force = getenv("TPL_GEMM_PAIR");
-  const int64_t fk = force ? (force[0] == '1' ? 2 : 1) : (getenv("TPL_GEMM_TILE") ? 3 : 0);
+  const char* ftile = getenv("TPL_GEMM_PAIR_TILE");
+  const int64_t fk = (force ? (force[0] == '1' ? 2 : 1) : (getenv("TPL_GEMM_TILE") ? 3 : 0)) +
+                     4 * (ftile ? (int64_t)atoi(ftile) : 0);
   const int64_t flags = (dg.a_kmajor ? 1 : 0) | (dg.b_kmajor ? 2 : 0) | (dg.c_f32 ? 4 : 0) | (wg.a_kmajor ? 8 : 0) |
                         (wg.b_kmajor ? 16 : 0) | (wg.c_f32 ? 32 : 0) | (int64_t)(wg.ldc == wg.N) << 6 |
                         (int64_t)dg.dtype << 8 | (int64_t)wg.dtype << 12 | (int64_t)dg.epi << 16 |
@@ -1963,7 +2020,8 @@ hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, const PairPl
   if (dg.dtype != DT_BF16 || wg.dtype != DT_BF16 || plan.wg_splits < 1 || plan.dg_splits < 1) return hipErrorInvalidValue;
   if (plan.dg_splits > 1 && dg.epi != EPI_NONE) return hipErrorInvalidValue;
   if ((plan.wg_splits > 1 || plan.dg_splits > 1 || dg.epi == EPI_DGELU) && !ws) return hipErrorInvalidValue;
-  Args a0 = pair_args(dg), a1 = pair_args(wg);
+  if (plan.tile != 256 && (plan.tile != 128 || dg.epi != EPI_NONE)) return hipErrorInvalidValue;
+  Args a0 = pair_args(dg, plan.tile), a1 = pair_args(wg, plan.tile);
   a0.colpart = dg.epi == EPI_DGELU ? ws : nullptr;
   const bool dsplit = plan.dg_splits > 1;
   if (dsplit) {   // every split of dg into fp32 slices: slice 0 at ws, slice s at ws + s*M*N
@@ -1983,8 +2041,23 @@ hipError_t launch_gemm_pair(const GemmDesc& dg, const GemmDesc& wg, const PairPl
   const bool wg_first = a1.kchunk > a0.kchunk;   // the longer tiles start first
   const int n0 = (int)(wg_first ? t1 : t0), n0pad = (n0 + 7) / 8 * 8, n1 = (int)(wg_first ? t0 : t1);
   if (n0 + n1 == 0) return hipSuccess;
-  const dim3 grid((unsigned)(n0pad + n1)), block(512);
-  if (dsplit) {   // both products on the 2 x 4 wave layout with fp32 output
+  const dim3 grid((unsigned)(n0pad + n1)), block(plan.tile == 128 ? 256 : 512);
+  if (plan.tile == 128) {
+    if (dsplit) {
+      if (wg_first)
+        hipLaunchKernelGGL((gemm_pair128_kernel<false, false, float, true, false, float>), grid, block, 0, s, a1, a0, n0,
+                           n0pad);
+      else
+        hipLaunchKernelGGL((gemm_pair128_kernel<true, false, float, false, false, float>), grid, block, 0, s, a0, a1, n0,
+                           n0pad);
+    } else if (wg_first) {
+      hipLaunchKernelGGL((gemm_pair128_kernel<false, false, float, true, false, bf16>), grid, block, 0, s, a1, a0, n0,
+                         n0pad);
+    } else {
+      hipLaunchKernelGGL((gemm_pair128_kernel<true, false, bf16, false, false, float>), grid, block, 0, s, a0, a1, n0,
+                         n0pad);
+    }
+  } else if (dsplit) {   // both products on the 2 x 4 wave layout with fp32 output
     if (wg_first)
       hipLaunchKernelGGL((gemm_pair_kernel<2, 4, false, false, EPI_NONE, float, 2, 4, true, false, EPI_NONE, float>),
                          grid, block, 0, s, a1, a0, n0, n0pad);

@@ -61,13 +61,14 @@ struct GemmDesc {
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t s);
 // A block's activation-gradient product dg (A K-major, B MN-major, storage
 // type out, EPI_NONE or EPI_DGELU) and its weight-gradient product wg (both
-// MN-major, fp32 out, ldc == N) in one launch on 256x256 tiles, wg and an
-// EPI_NONE dg possibly split over K inside it. gemm_pair_plan says whether
+// MN-major, fp32 out, ldc == N) in one launch on 256x256 tiles (or 128x128
+// ones for an EPI_NONE dg: plan.tile), wg and an EPI_NONE dg possibly split
+// over K inside it. gemm_pair_plan says whether
 // that beats two launches (and fills *plan either way); the launch then needs
 // gemm_pair_ws_floats of workspace: an EPI_DGELU dg's
 // gemm_pair_colpart_chunks(dg.M) column partials (dg.colpart is ignored:
 // they go to ws) or a split dg's fp32 slices first, then wg's split slices.
-struct PairPlan { int dg_splits, dg_kchunk, wg_splits, wg_kchunk; };
+struct PairPlan { int dg_splits, dg_kchunk, wg_splits, wg_kchunk; int tile = 256; };   // tile: 256 or 128
 bool gemm_pair_plan(const GemmDesc& dg, const GemmDesc& wg, PairPlan* plan);
 int64_t gemm_pair_colpart_chunks(int64_t M);
 size_t gemm_pair_ws_floats(const GemmDesc& dg, const GemmDesc& wg, const PairPlan& plan);

@@ -132,15 +132,17 @@ PAIR_SPLITS = synth.tiny_config("bf16", hidden=1152, heads=9, head_dim=128, ffn=
                                 name="small_bf16_pair_splits")
 
 
-@pytest.mark.parametrize("pair", ["0", "1"])
+@pytest.mark.parametrize("pair,tile", [("0", "256"), ("1", "256"), ("1", "128")])
 @pytest.mark.parametrize("cfg", [SMALL[1], SMALL[2], SMALL[3], PAIR_SPLITS], ids=lambda c: c.name)
-def test_paired_backward_products(cfg, pair, monkeypatch):
+def test_paired_backward_products(cfg, pair, tile, monkeypatch):
     """Each block's activation- and weight-gradient products in one launch
     (chosen automatically where it fills the CUs better, e.g. the 175B rank;
-    forced on and off here on ragged shapes, with the fc2 pair's GeLU'
+    forced on and off here on ragged shapes, on 256x256 tiles and, for the
+    pairs without an epilogue, on 128x128 tiles, with the fc2 pair's GeLU'
     epilogue and bias-gradient column partials, and with splits over K and
     the follow-on launch's sums on the deeper case)."""
     monkeypatch.setenv("TPL_GEMM_PAIR", pair)
+    monkeypatch.setenv("TPL_GEMM_PAIR_TILE", tile)
     report, st = check_case(cfg)
     _assert_ok(report)
 
