@@ -445,6 +445,10 @@ def summarize_profiles(d: str, workload: str, trace_only: bool = False):
              f"Calibration: a {copy_bytes >> 20} MiB device copy reads and writes {copy_bytes >> 20} MiB; the counters "
              f"read FETCH x{1 / scale['FETCH_SIZE']:.3f}, WRITE x{1 / scale['WRITE_SIZE']:.3f} of that, so bench "
              f"bytes are scaled by {scale['FETCH_SIZE']:.3f} (fetch) and {scale['WRITE_SIZE']:.3f} (write).", "",
+             "The counters see the L2's requests to the memory side: a fetch served by the 256 MB "
+             "last-level cache (MALL) counts like one from HBM, so fetch figures above a kernel's "
+             "algorithmic reads are L2 misses (operand panels re-read by other XCDs or after "
+             "eviction), not necessarily HBM transfers.", "",
              "| family | fetch MB/launch | write MB/launch | kernel source sha256 |", "|---|---|---|---|"]
     for f, v in sorted(traffic.items(), key=lambda kv: -kv[1]["bytes_per_launch"]):
         lines.append(f"| {f} | {v['fetch_bytes_per_launch'] / 1e6:.1f} | {v['write_bytes_per_launch'] / 1e6:.1f} | "
